@@ -1,0 +1,204 @@
+/*
+ * pa.h — C ABI of libpa.so: paged decode attention and the two KV-cache kernels for
+ * AMD MI355X (gfx950).
+ *
+ * The problem, as the pages state it: the K/V cache of every sequence lives in fixed-size
+ * blocks of one physical pool; a per-sequence block table maps logical blocks, in order, to
+ * non-contiguous physical blocks; the attention kernel reads K/V block by block through that
+ * table (UltraLAB summary of Kwon et al., SOSP 2023 (xasun.com), sections 一 and 二;
+ * "GPT-OSS显存管理技巧：PagedAttention机制解析" (yongjin360.com) §2.2; PyTorch-CUDA-v2.9
+ * PagedAttention page (jsqmd.com), paged-memory section).  What is computed per query head is
+ * scaled dot-product attention with a softmax ("PagedAttention技术：加速GPT推理的利器"
+ * (yunthe.com) §1.1).
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller; the library keeps no
+ *     pointer after it returns and allocates no device memory.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the default
+ *     stream) and the call returns without waiting.  The caller keeps every buffer alive
+ *     until the stream has finished.  Calls on one stream run in order, so
+ *     copy_blocks -> reshape_and_cache -> decode on one stream sees each write.
+ *   - Every array is dense, row-major, with the shapes given below.
+ *   - Problems that the host can see (null pointers, unsupported sizes, a short workspace)
+ *     return an error code before anything is launched; nothing aborts and no C++ exception
+ *     crosses this boundary.  Device-array contents are preconditions and are not checked
+ *     on the host (that would need a synchronisation); the kernels still guard every index
+ *     so that a bad one is skipped instead of read or written out of bounds.
+ *   - `num_seqs`, `num_tokens` or `num_pairs` equal to 0 is a successful no-op.
+ *   - The library is stateless apart from cached device properties; calls are thread-safe.
+ *
+ * Element types: `pa_dtype` selects the element type of q, out, key, value and both pools
+ * (all of one call share it).  Arithmetic is fp32 in every kernel.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  PA_ERR_BAD_SHAPE = 2,    /* a size is negative, zero where it must not be, or inconsistent */
+  PA_ERR_UNSUPPORTED = 3,  /* a valid but unsupported combination (head_dim, block_size, dtype) */
+  PA_ERR_WORKSPACE = 4,    /* the workspace is missing or smaller than required */
+  PA_ERR_LAUNCH = 5        /* the HIP runtime reported an error when launching */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Kernel family for pa_decode_ex.  PA_KERNEL_AUTO is what pa_decode uses. */
+typedef enum {
+  PA_KERNEL_AUTO = 0,
+  PA_KERNEL_VALU = 1,  /* vector-ALU kernel: any head grouping, every dtype */
+  PA_KERNEL_MFMA = 2   /* matrix-core kernel for grouped-query attention (f16/bf16) */
+} pa_kernel;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_string(pa_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t pa_version(void);
+
+/*
+ * Partition length, in tokens, that pa_decode uses for split-KV when the caller passes
+ * partition_size = 0.  Depends only on host scalars.  Returns 0 for invalid arguments.
+ */
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq);
+
+/*
+ * Bytes of workspace pa_decode needs for this shape (0 when no split is needed).  The
+ * workspace holds, per (sequence, query head, partition), the fp32 running max, the fp32
+ * softmax denominator and the fp32 normalised partial output [head_dim]; the merge kernel
+ * combines them by their log-sum-exp weights.  `partition_size` as for pa_decode.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t partition_size);
+
+/*
+ * pa_decode — single-query paged decode attention.
+ *
+ * For every sequence s and query head h, with n = context_lens[s], G = num_heads /
+ * num_kv_heads and KV head g = h / G (contiguous groups):
+ *   K_t = key_cache[block_tables[s][t / block_size]][g][t % block_size][:]  (t < n), V alike
+ *   z_t = scale * <query[s][h], K_t>
+ *   out[s][h] = sum_t softmax(z)_t * V_t          (max-subtracted softmax, fp32 throughout)
+ * and out[s][h] = 0 when n <= 0.  Paging changes where K/V live, not the result (the
+ * xasun.com summary, section 一, calls the scheme lossless).
+ *
+ *   out           [num_seqs][num_heads][head_dim]                   dtype   (written)
+ *   query         [num_seqs][num_heads][head_dim]                   dtype
+ *   key_cache     [num_blocks][num_kv_heads][block_size][head_dim]  dtype
+ *   value_cache   same as key_cache
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries j < ceil(n/block_size) must
+ *                 be in [0, num_blocks); later entries are never read
+ *   context_lens  int32 [num_seqs]; tokens cached for the sequence, including the one being
+ *                 decoded; must be <= max_blocks_per_seq * block_size (larger is clamped)
+ *   scale         softmax scale (fp32), typically 1/sqrt(head_dim)
+ *   partition_size  tokens per split-KV partition: 0 = library choice
+ *                 (pa_decode_auto_partition), otherwise a positive multiple of block_size;
+ *                 a partition size covering the whole table means a single pass
+ *   workspace     device buffer of at least pa_decode_workspace_bytes(...) bytes (may be
+ *                 NULL when that is 0); contents on entry are ignored
+ *
+ * Supported: head_dim in {64, 128}; block_size in {16, 32}; num_heads a multiple of
+ * num_kv_heads; every pa_dtype.  Slots past a sequence's context, unused blocks and unused
+ * table entries are never read as values, so they may hold anything (NaN included).
+ * Errors: PA_ERR_NULL_PTR, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
+ * PA_ERR_LAUNCH.
+ */
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    float scale, pa_dtype dtype, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_ex — pa_decode with an explicit kernel family.  PA_KERNEL_MFMA requires
+ * dtype f16/bf16 and num_heads / num_kv_heads in {4, 8, 16} (PA_ERR_UNSUPPORTED otherwise);
+ * PA_KERNEL_VALU accepts every supported shape.  Same arguments, results and errors as
+ * pa_decode otherwise.
+ */
+pa_status pa_decode_ex(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                       pa_dtype dtype, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, pa_kernel kernel, void* stream);
+
+/*
+ * The two launches of pa_decode, exposed so a caller (or a profiler harness) can bracket
+ * each with its own events.  pa_decode == pa_decode_partitions followed by pa_decode_merge
+ * on the same stream with the same arguments.  pa_decode_partitions writes `out` directly
+ * for every (sequence, head) whose context fits one partition and fp32 partials to the
+ * workspace for the others; pa_decode_merge combines those partials into `out` and leaves
+ * the rest of `out` alone.
+ */
+pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                               pa_dtype dtype, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, pa_kernel kernel, void* stream);
+
+pa_status pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype,
+                          int32_t partition_size, const void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * pa_reshape_and_cache — store each new token's K and V at its physical slot.
+ *
+ * Every decode step appends the new token's key/value to its sequence's cache (jsqmd.com
+ * page, paged-memory section and serving-workflow list).  For token i with
+ * slot = slot_mapping[i] >= 0:  block = slot / block_size, offset = slot % block_size and
+ *   key_cache[block][h][offset][:] = key[i][h][:]   for every KV head h (value alike).
+ * Bits are copied unchanged.  A negative slot is skipped (padding); a slot >= num_blocks *
+ * block_size is skipped as out of range.  Slots must be distinct (otherwise which token wins
+ * is unspecified).
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim]  dtype
+ *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim]  (updated in place)
+ *   slot_mapping  int64 [num_tokens]
+ * Supported: head_dim * sizeof(dtype) a multiple of 16 bytes, head_dim <= 1024; block_size >= 1.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * pa_copy_blocks — copy-on-write block copies.
+ *
+ * Blocks shared between sequences are reference-counted and copied before one of the
+ * sharers writes (xasun.com summary, sections 一 and 二, sharing item).  For each pair
+ * p, with (src, dst) = (block_mapping[2p], block_mapping[2p+1]), the whole of block src —
+ * every KV head and every slot — is copied to block dst, in both pools.  Pairs with an id
+ * outside [0, num_blocks) are skipped.  Destinations must be distinct and must not be a
+ * source of another pair (true of copy-on-write, which copies into fresh blocks); under that
+ * condition the result does not depend on the order of the pairs.
+ *
+ *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim]  (updated in place)
+ *   block_mapping  int64 [num_pairs][2]
+ * Supported: num_kv_heads * block_size * head_dim * sizeof(dtype) a multiple of 16 bytes.
+ */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,18 @@
+"""CPU oracle for paged decode attention — test infrastructure only.
+
+Only the test-suite, the smoke check in ``__graft_entry__`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It imports nothing from the GPU library.
+"""
+
+from .pa_oracle import (  # noqa: F401
+    copy_blocks_ref,
+    decode_ref,
+    decode_split_ref,
+    f64_to_storage,
+    kv_bytes_per_token,
+    num_blocks_for,
+    reshape_and_cache_ref,
+    resolve_sequence,
+    slot_utilization,
+    storage_to_f64,
+)

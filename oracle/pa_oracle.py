@@ -1,0 +1,264 @@
+"""Plain float64 CPU oracle for paged decode attention, reshape_and_cache and copy_blocks.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import, call or run anything here.  The GPU library never calls it,
+and nothing here imports the GPU library.  It is deliberately slow: one sequence and one
+head at a time, no blocking, no fusion, no reordering.
+
+What is computed, and where the pages say so
+--------------------------------------------
+* Paged KV cache: K and V of each sequence live in fixed-size blocks of a shared physical
+  pool; a per-sequence block table maps logical block j (tokens j*bs .. j*bs+bs-1) to a
+  physical block.  PyTorch-CUDA-v2.9 PagedAttention page (jsqmd.com), section on paged memory
+  for the KV cache; "GPT-OSS显存管理技巧：PagedAttention机制解析" (yongjin360.com) §2.2;
+  UltraLAB summary of Kwon et al., SOSP 2023 (xasun.com) §一.
+* The attention kernel fetches K/V block by block through the block table (xasun.com summary
+  §二, attention-algorithm item), and paging does not change the result (same page, §一,
+  "lossless" claim).  So the oracle resolves the table into contiguous K/V and then applies
+  the plain definition.
+* The definition is scaled dot-product attention with a softmax over the scores
+  ("PagedAttention技术：加速GPT推理的利器" (yunthe.com) §1.1).  For one decoded query:
+      z_t = scale * <q, k_t>,   p_t = exp(z_t - max z) / sum_u exp(z_u - max z),
+      out = sum_t p_t v_t.
+* Each decode step appends the new token's K/V into the cache (jsqmd.com page, paged-memory
+  section and serving-workflow list).  reshape_and_cache_ref writes it at its physical slot.
+* Blocks shared between sequences are reference-counted and copied before a write
+  (copy-on-write; xasun.com summary §一 and §二, sharing item).  copy_blocks_ref is that copy.
+* Per-token KV size (xasun.com summary §三, memory-capacity row: about 800 KB per token for
+  OPT-13B) and block counts (yunthe.com §1.2: 2048 tokens in 128-token pages is 16 pages).
+
+Readings where the pages are silent (each is listed with its reason in the design notes):
+* ``scale`` is a caller argument (1/sqrt(head_dim) in every workload).
+* ``context_lens`` counts the token being decoded (its K/V is written first).
+* A context of 0 tokens gives an all-zero output (softmax over an empty set is undefined).
+* Grouped-query attention maps query head h to KV head floor(h / G), G = Hq / Hkv.
+* Slots past the context, unused blocks and unused table entries are never read.
+* Split-KV partitions cover tokens [p*P, min((p+1)*P, n)) and are merged by their
+  log-sum-exp weights; exact arithmetic gives the unsplit result.
+* A slot or block id outside the pool is skipped by the cache writers.
+
+Parity pins (``tests/test_oracle_pins.py``): brute-force contiguous attention and torch's
+float64 SDPA on tiny inputs; paged == contiguous; invariance under any permutation of the
+physical placement; all-equal keys and scale 0 give mean(V); one-token context gives V
+exactly; poisoned unused slots/blocks/table entries change nothing; split+merge == unsplit;
+the pages' per-token KV and page-count arithmetic (``tests/golden/``); reshape/copy against a
+flat-slot formulation and a per-element loop; copy-on-write round trips.  A mutation test
+plants mistakes in a copy of this file and checks that some pin fails for each.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_BF16_MIN_EXP = -133  # quantum of bfloat16 subnormals: 2**-133
+
+
+# ---------------------------------------------------------------------------------------
+# element types
+# ---------------------------------------------------------------------------------------
+def storage_to_f64(x, dtype: str) -> np.ndarray:
+    """Exact float64 value of a storage array ("f32": float32, "f16": float16,
+    "bf16": uint16 raw bits)."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(x).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(x).view(np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 to bfloat16 (nearest, ties to even) in one step: scale each value so
+    its bfloat16 quantum is 1, round with rint (ties-to-even), scale back."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    _, e = np.frexp(xf)                       # xf = m * 2**e, 0.5 <= |m| < 1
+    qexp = np.maximum(e - 8, _BF16_MIN_EXP)   # 8 significant bits for normal values
+    r = np.ldexp(np.rint(np.ldexp(xf, -qexp)), qexp)
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)            # exact, or +-inf past the bfloat16 range
+    bits = (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    big = np.abs(r) >= 2.0 ** 128
+    bits = np.where(big, np.where(r > 0, np.uint16(0x7F80), np.uint16(0xFF80)), bits)
+    out[...] = bits
+    out[np.isnan(x)] = 0x7FC0
+    out[np.isposinf(x)] = 0x7F80
+    out[np.isneginf(x)] = 0xFF80
+    return out
+
+
+def f64_to_storage(x, dtype: str) -> np.ndarray:
+    """Round float64 to the storage type, nearest-even, in a single rounding."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        return _f64_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------------------
+# paging arithmetic
+# ---------------------------------------------------------------------------------------
+def num_blocks_for(num_tokens: int, block_size: int) -> int:
+    """Blocks a sequence of ``num_tokens`` occupies: ceil(n / bs)."""
+    return -(-int(num_tokens) // int(block_size))
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """K and V of one token across all layers: 2 * L * H_kv * d * e bytes."""
+    return 2 * int(num_layers) * int(num_kv_heads) * int(head_dim) * int(elem_bytes)
+
+
+def slot_utilization(lengths, block_size: int) -> float:
+    """Fraction of reserved slots holding a token: sum(n) / sum(ceil(n/bs) * bs)."""
+    lengths = [int(n) for n in lengths]
+    reserved = sum(num_blocks_for(n, block_size) * block_size for n in lengths)
+    return sum(lengths) / reserved if reserved else 1.0
+
+
+def resolve_sequence(cache, table_row, num_tokens: int, block_size: int, dtype: str) -> np.ndarray:
+    """Logical K (or V) of one sequence: float64 ``[H_kv, n, d]``.
+
+    Follows the block table: logical block j is physical block ``table_row[j]``; within a
+    block, token t sits at offset t mod bs.  Only the first ceil(n/bs) table entries are
+    read, and only the first n tokens are kept.
+    """
+    n = int(num_tokens)
+    nb = num_blocks_for(n, block_size)
+    phys = np.asarray(table_row[:nb], dtype=np.int64)
+    blocks = storage_to_f64(cache[phys], dtype)          # [nb, H, bs, d]
+    h, d = blocks.shape[1], blocks.shape[3]
+    seq = blocks.transpose(1, 0, 2, 3).reshape(h, nb * block_size, d)
+    return seq[:, :n, :]
+
+
+# ---------------------------------------------------------------------------------------
+# decode attention
+# ---------------------------------------------------------------------------------------
+def _softmax_weighted_sum(K, V, q, scale):
+    """Attention of one query over n keys/values (all float64)."""
+    z = scale * (K @ q)
+    z = z - z.max()
+    p = np.exp(z)
+    return (p @ V) / p.sum()
+
+
+def decode_ref(query, key_cache, value_cache, block_tables, context_lens, block_size, scale,
+               dtype: str) -> np.ndarray:
+    """Single-query paged decode attention, float64 ``[S, Hq, d]``.
+
+    ``query`` [S, Hq, d], ``key_cache``/``value_cache`` [NB, Hkv, bs, d] (storage arrays),
+    ``block_tables`` [S, max_blocks], ``context_lens`` [S], ``scale`` a float32 value.
+    """
+    S, Hq, d = query.shape
+    Hkv = key_cache.shape[1]
+    if Hq % Hkv:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    out = np.zeros((S, Hq, d), dtype=np.float64)
+    for s in range(S):
+        n = int(context_lens[s])
+        if n <= 0:
+            continue
+        K = resolve_sequence(key_cache, block_tables[s], n, block_size, dtype)
+        V = resolve_sequence(value_cache, block_tables[s], n, block_size, dtype)
+        q = storage_to_f64(query[s], dtype)
+        for h in range(Hq):
+            kv = h // G
+            out[s, h] = _softmax_weighted_sum(K[kv], V[kv], q[h], sc)
+    return out
+
+
+def decode_split_ref(query, key_cache, value_cache, block_tables, context_lens, block_size, scale,
+                     dtype: str, partition_size: int):
+    """Split-KV decode: per partition (m, l, o) then a log-sum-exp merge.
+
+    Partition p of a sequence with n tokens covers tokens [p*P, min((p+1)*P, n)).  For each
+    partition: m = max z, l = sum exp(z - m), o = sum exp(z - m) v / l.  Merge:
+    M = max_p m_p, w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p.
+    Returns (out [S, Hq, d], partials) with partials[s][h] a list of (m, l, o).
+    """
+    S, Hq, d = query.shape
+    Hkv = key_cache.shape[1]
+    G = Hq // Hkv
+    P = int(partition_size)
+    if P <= 0:
+        raise ValueError("partition_size must be positive")
+    sc = float(np.float32(scale))
+    out = np.zeros((S, Hq, d), dtype=np.float64)
+    partials = []
+    for s in range(S):
+        n = int(context_lens[s])
+        row = []
+        if n <= 0:
+            partials.append([[] for _ in range(Hq)])
+            continue
+        K = resolve_sequence(key_cache, block_tables[s], n, block_size, dtype)
+        V = resolve_sequence(value_cache, block_tables[s], n, block_size, dtype)
+        q = storage_to_f64(query[s], dtype)
+        for h in range(Hq):
+            kv = h // G
+            parts = []
+            for t0 in range(0, n, P):
+                t1 = min(t0 + P, n)
+                z = sc * (K[kv, t0:t1] @ q[h])
+                m = z.max()
+                e = np.exp(z - m)
+                l = e.sum()
+                parts.append((m, l, (e @ V[kv, t0:t1]) / l))
+            M = max(m for m, _, _ in parts)
+            w = np.array([l * math.exp(m - M) for m, l, _ in parts])
+            o = np.stack([o for _, _, o in parts])
+            out[s, h] = (w @ o) / w.sum()
+            row.append(parts)
+        partials.append(row)
+    return out, partials
+
+
+# ---------------------------------------------------------------------------------------
+# cache writers
+# ---------------------------------------------------------------------------------------
+def reshape_and_cache_ref(key, value, key_cache, value_cache, slot_mapping, block_size):
+    """Copies of the pools with token i's K/V [Hkv, d] stored at physical slot
+    ``slot_mapping[i]``: block slot // bs, offset slot % bs.  Negative or out-of-pool slots
+    are skipped.  Bits are copied unchanged."""
+    kc = np.array(key_cache, copy=True)
+    vc = np.array(value_cache, copy=True)
+    nb = kc.shape[0]
+    bs = int(block_size)
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        slot = int(slot)
+        if slot < 0 or slot >= nb * bs:
+            continue
+        b, o = divmod(slot, bs)
+        kc[b, :, o, :] = key[i]
+        vc[b, :, o, :] = value[i]
+    return kc, vc
+
+
+def copy_blocks_ref(key_cache, value_cache, block_mapping):
+    """Copies of the pools where block dst receives the whole of block src (every head,
+    every slot) for each (src, dst) pair, all read from the pools as they were before the
+    call.  Pairs with an id outside the pool are skipped."""
+    k0 = np.array(key_cache, copy=True)
+    v0 = np.array(value_cache, copy=True)
+    kc = np.array(key_cache, copy=True)
+    vc = np.array(value_cache, copy=True)
+    nb = kc.shape[0]
+    for src, dst in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        src, dst = int(src), int(dst)
+        if not (0 <= src < nb and 0 <= dst < nb):
+            continue
+        kc[dst] = k0[src]
+        vc[dst] = v0[src]
+    return kc, vc

@@ -1,0 +1,75 @@
+"""Every plausible mistake planted in a copy of the oracle must make some pin fail.
+
+The real oracle file is never modified: its source is read, one substring is replaced, and
+the result is executed as a fresh module that the pins then run against.
+"""
+
+import pathlib
+import types
+
+import pytest
+
+import oracle_pins
+
+SRC = (pathlib.Path(__file__).resolve().parents[1] / "oracle" / "pa_oracle.py").read_text()
+
+# (name, original substring, planted mistake)
+MUTATIONS = [
+    ("dropped scale", "z = scale * (K @ q)", "z = (K @ q)"),
+    ("wrong GQA head map", "            kv = h // G\n            out[s, h]",
+     "            kv = h % Hkv\n            out[s, h]"),
+    ("wrong query head", "_softmax_weighted_sum(K[kv], V[kv], q[h], sc)",
+     "_softmax_weighted_sum(K[kv], V[kv], q[kv], sc)"),
+    ("token/block order transposed", "seq = blocks.transpose(1, 0, 2, 3)",
+     "seq = blocks.transpose(1, 2, 0, 3)"),
+    ("table read off by one", "phys = np.asarray(table_row[:nb]", "phys = np.asarray(table_row[1:nb + 1]"),
+    ("context shifted", "return seq[:, :n, :]", "return seq[:, 1:n + 1, :]"),
+    ("floor block count", "    nb = num_blocks_for(n, block_size)\n    phys",
+     "    nb = max(1, n // block_size)\n    phys"),
+    ("unstable shift", "z = z - z.max()\n    p = np.exp(z)", "z = z - z.min()\n    p = np.exp(z)"),
+    ("exp sign", "    p = np.exp(z)\n    return", "    p = np.exp(-z)\n    return"),
+    ("wrong normaliser", "return (p @ V) / p.sum()", "return (p @ V) / p.max()"),
+    ("keys used as values", "return (p @ V) / p.sum()", "return (p @ K) / p.sum()"),
+    ("empty context not handled", "        if n <= 0:\n            continue\n        K = resolve",
+     "        K = resolve"),
+    ("divmod swapped", "b, o = divmod(slot, bs)", "o, b = divmod(slot, bs)"),
+    ("negative slot written", "if slot < 0 or slot >= nb * bs:", "if slot >= nb * bs:"),
+    ("value not written", "        vc[b, :, o, :] = value[i]\n", "        vc[b, :, o, :] = key[i]\n"),
+    ("copy direction", "kc[dst] = k0[src]", "kc[src] = k0[dst]"),
+    ("V block not copied", "        vc[dst] = v0[src]\n", "        pass\n"),
+    ("bf16 truncation", "r = np.ldexp(np.rint(", "r = np.ldexp(np.trunc("),
+    ("bf16 precision", "qexp = np.maximum(e - 8,", "qexp = np.maximum(e - 9,"),
+    ("bf16 decode shift", "<< np.uint32(16)\n        return bits", "<< np.uint32(15)\n        return bits"),
+    ("merge weight", "w = np.array([l * math.exp(m - M) for m, l, _ in parts])",
+     "w = np.array([l for m, l, _ in parts])"),
+    ("partition bound", "t1 = min(t0 + P, n)", "t1 = min(t0 + P - 1, n)"),
+    ("kv bytes factor", "return 2 * int(num_layers)", "return int(num_layers)"),
+    ("floor page count", "return -(-int(num_tokens) // int(block_size))",
+     "return int(num_tokens) // int(block_size)"),
+    ("utilisation denominator", "reserved = sum(num_blocks_for(n, block_size) * block_size for n in lengths)",
+     "reserved = sum(lengths)"),
+]
+
+
+def _mutant(orig, new):
+    assert SRC.count(orig) == 1, f"mutation anchor must occur exactly once: {orig!r}"
+    mod = types.ModuleType("pa_oracle_mutant")
+    exec(compile(SRC.replace(orig, new), "pa_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,orig,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(name, orig, new):
+    mod = _mutant(orig, new)
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:
+            return
+    pytest.fail(f"no pin caught the planted mistake: {name}")
+
+
+def test_unmutated_copy_passes():
+    mod = _mutant("z = scale * (K @ q)", "z = scale * (K @ q)")
+    for pin in oracle_pins.ALL_PINS:
+        pin(mod)
