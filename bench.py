@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged-KV decode step on one MI355X, printed as one JSON line.
+
+A step is the whole hot path over one batch: copy_blocks (copy-on-write pairs, none in the
+Llama-7B workload) -> reshape_and_cache (one new token per sequence) -> pa_decode (partition
+kernel + log-sum-exp merge).  Inputs are seeded synthetic data drawn on the GPU before timing.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama7b_bs16]
+
+The reported value is the step's algorithmic bytes divided by the step time (GB/s).  The
+`roofline` object covers the dominant kernel (the decode partition kernel), timed with HIP
+events on the stream it runs on; `cpu_baseline` times the float64 CPU oracle on a bounded
+sample of the same workload.  `--calibrate-copy` instead times copy_blocks on a known number
+of bytes (the reference copy used to scale hardware byte counters).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+import numpy as np
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+from paged_kv_cache_05_amd import ops  # noqa: E402
+from paged_kv_cache_05_amd import workloads as W  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, AMD's published peak
+METRIC = "paged decode attention achieved HBM GB/s (% of MI355X peak) + seq-heads/s"
+TRAFFIC_FILE = ROOT / "profiles" / "decode_traffic.json"
+KERNEL_SOURCES = {
+    "valu": ["pa_decode_valu.hip", "pa_common.h"],
+    "mfma": ["pa_decode_mfma.hip", "pa_common.h"],
+}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update((ROOT / "paged_kv_cache_05_amd" / "csrc" / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(case) -> int:
+    """Algorithmic HBM bytes of one decode call: every live K and V row once, q in, out, the
+    table entries read and the context lengths."""
+    sp = case.spec
+    e = W.ELEM_BYTES[sp.dtype]
+    n = case.context_lens.astype(np.int64)
+    kv = int(n.sum()) * sp.num_kv_heads * sp.head_dim * e * 2
+    qo = sp.num_seqs * sp.num_heads * sp.head_dim * e * 2
+    tables = int((-(-n // sp.block_size)).sum()) * 4 + 4 * sp.num_seqs
+    return kv + qo + tables
+
+
+def cache_write_bytes(case) -> int:
+    sp = case.spec
+    e = W.ELEM_BYTES[sp.dtype]
+    row = sp.num_kv_heads * sp.head_dim * e
+    reshape = len(case.slot_mapping) * (row * 2 * 2 + 8)               # read new K,V; write both
+    block = sp.num_kv_heads * sp.block_size * sp.head_dim * e
+    copy = len(case.block_mapping) * (block * 2 * 2 + 16)               # read+write K and V blocks
+    return reshape + copy
+
+
+def chosen_kernel(case, requested: str) -> str:
+    sp = case.spec
+    if requested != "auto":
+        return requested
+    G = sp.num_heads // sp.num_kv_heads
+    return "mfma" if (sp.dtype in ("f16", "bf16") and sp.head_dim == 128 and G % 4 == 0) else "valu"
+
+
+class Step:
+    def __init__(self, case, dev, kernel="auto"):
+        import torch
+        self.case = case
+        sp = case.spec
+        dt = sp.dtype
+        self.kernel = kernel
+        self.q = W.to_torch(case.query, dt, dev)
+        self.kc, self.vc = case.key_cache, case.value_cache
+        self.bt = torch.from_numpy(case.block_tables).to(dev)
+        self.cl = torch.from_numpy(case.context_lens).to(dev)
+        self.nk = W.to_torch(case.new_key, dt, dev)
+        self.nv = W.to_torch(case.new_value, dt, dev)
+        self.slots = torch.from_numpy(case.slot_mapping).to(dev)
+        self.pairs = torch.from_numpy(case.block_mapping.reshape(-1, 2)).to(dev)
+        self.out = torch.empty_like(self.q)
+        self.P = sp.partition_size
+        nbytes = ops.workspace_bytes(sp.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim,
+                                     sp.block_size, case.max_blocks_per_seq, self.P)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def run(self, ev=None):
+        if len(self.case.block_mapping):
+            ops.copy_blocks(self.kc, self.vc, self.pairs)
+        ops.reshape_and_cache(self.nk, self.nv, self.kc, self.vc, self.slots)
+        if ev is not None:
+            ev[0].record()
+        ops.decode_partitions(self.out, self.q, self.kc, self.vc, self.bt, self.cl,
+                              float(self.case.scale), self.ws, partition_size=self.P,
+                              kernel=self.kernel)
+        if ev is not None:
+            ev[1].record()
+        ops.decode_merge(self.out, self.cl, self.case.spec.num_kv_heads, self.case.spec.block_size,
+                         self.case.max_blocks_per_seq, self.ws, partition_size=self.P)
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step.run(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    kern = [a.elapsed_time(b) for a, b in evs]
+    return total_ms / steps, float(np.mean(kern)), float(np.min(kern)), wall
+
+
+def snapshot_sequences(case, seqs):
+    """Host copies of the blocks the given sequences read (taken before any step runs)."""
+    import torch
+    bs = case.block_size
+    out = []
+    for s in seqs:
+        n = int(case.context_lens[s])
+        row = case.block_tables[s, : -(-n // bs)].astype(np.int64)
+        idx = torch.from_numpy(row).to(case.key_cache.device)
+        out.append((s, n, W.from_torch(case.key_cache.index_select(0, idx), case.dtype),
+                    W.from_torch(case.value_cache.index_select(0, idx), case.dtype)))
+    return out
+
+
+def cpu_baseline(case, snaps, budget_s):
+    """The float64 oracle decoding the snapshotted sequences one at a time (BLAS limited to one
+    thread), cycling over them until at least one full pass and ``budget_s`` seconds are done."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    sp = case.spec
+    bs = case.block_size
+    e = W.ELEM_BYTES[sp.dtype]
+    prepared = []
+    for s, n, mk, mv in snaps:
+        table = np.arange(mk.shape[0], dtype=np.int32)[None]
+        slot = np.array([n - 1], np.int64)   # the new token: last slot of the sequence
+        mk, mv = oracle.reshape_and_cache_ref(case.new_key[s:s + 1], case.new_value[s:s + 1],
+                                              mk, mv, slot, bs)   # the step's write (untimed)
+        prepared.append((s, n, mk, mv, table))
+    done, bytes_done, heads, tokens, elapsed = 0, 0, 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while done < len(prepared) or elapsed < budget_s:
+            s, n, mk, mv, table = prepared[done % len(prepared)]
+            t = time.perf_counter()
+            oracle.decode_ref(case.query[s:s + 1], mk, mv, table, np.array([n], np.int32), bs,
+                              case.scale, case.dtype)
+            elapsed += time.perf_counter() - t
+            bytes_done += n * sp.num_kv_heads * sp.head_dim * e * 2 + sp.num_heads * sp.head_dim * e * 2
+            heads += sp.num_heads
+            tokens += n
+            done += 1
+    return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seq_heads_per_s": round(heads / elapsed, 2),
+            "seconds": round(elapsed, 2),
+            "sample": f"{done} sequence decodes cycling over the {len(prepared)} sequences of the "
+                      f"step ({tokens} cached tokens read, all {sp.num_heads} heads each), numpy "
+                      f"float64, one BLAS thread"}
+
+
+def traffic_for(kernel, workload):
+    if not TRAFFIC_FILE.exists():
+        return None
+    rec = json.loads(TRAFFIC_FILE.read_text())
+    entry = rec.get(workload, {})
+    if entry.get("kernel") != kernel or entry.get("kernel_source_sha") != kernel_source_sha(kernel):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(dev, steps):
+    """copy_blocks over 4096 distinct 128 KiB blocks (K and V): 1 GiB read + 1 GiB written."""
+    import torch
+    nb, shape = 8192, (8192, 32, 16, 128)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    pairs = torch.stack([torch.arange(0, nb // 2), torch.arange(nb // 2, nb)], 1).to(dev)
+    for _ in range(2):
+        ops.copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        ops.copy_blocks(kc, vc, pairs)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    moved = 2 * (nb // 2) * 32 * 16 * 128 * 2
+    print(json.dumps({"calibration": "copy_blocks", "read_bytes_per_launch": moved,
+                      "write_bytes_per_launch": moved, "ms_per_launch": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * moved / ms / 1e6, 1)}), flush=True)
+
+
+def run_workload(name, dev, steps, warmup, kernel):
+    import torch
+    case = W.build_case(W.CONFIGS[name], device=dev)
+    torch.cuda.synchronize()
+    step = Step(case, dev, kernel)
+    ms, kern_ms, kern_min, wall = time_steps(step, steps, warmup)
+    return case, step, ms, kern_ms, kern_min, wall
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
+    ap.add_argument("--also", default="llama7b_bs32",
+                    help="comma-separated extra workloads timed for the detail field ('' for none)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the paged decode step runs on a single MI355X and "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    ops.load()
+    if args.calibrate_copy:
+        calibrate_copy(dev, args.steps)
+        return 0
+
+    name = args.workload
+    case = W.build_case(W.CONFIGS[name], device=dev)
+    torch.cuda.synchronize()
+    snaps = None
+    if not args.no_cpu_baseline:
+        snaps = snapshot_sequences(case, range(case.spec.num_seqs))
+    step = Step(case, dev, args.kernel)
+    ms, kern_ms, kern_min, wall = time_steps(step, args.steps, args.warmup)
+    sp = case.spec
+    dbytes = decode_bytes(case)
+    sbytes = dbytes + cache_write_bytes(case)
+    kernel = chosen_kernel(case, args.kernel)
+    achieved = dbytes / (kern_ms * 1e-3) / 1e9
+    value = sbytes / (ms * 1e-3) / 1e9
+    P = sp.partition_size or ops.auto_partition(sp.num_seqs, sp.num_heads, sp.num_kv_heads,
+                                                sp.head_dim, sp.block_size, case.max_blocks_per_seq)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q on the GPU; lengths and placement per workload)",
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "seq_heads_per_s": round(sp.num_seqs * sp.num_heads / (ms * 1e-3), 1),
+        "config": {
+            "workload": name, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
+            "num_kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "block_size": sp.block_size,
+            "num_blocks": case.num_blocks, "context_lens": str(sp.lengths),
+            "mean_context": round(float(case.context_lens.mean()), 1),
+            "max_context": int(case.context_lens.max()), "partition": P, "kernel": kernel,
+            "step_bytes": sbytes, "decode_bytes": dbytes,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(kernel, name),
+            "kernel": f"decode_{kernel}_kernel", "avg_launch_ms": round(kern_ms, 4),
+            "min_launch_ms": round(kern_min, 4), "algorithmic_bytes_per_launch": dbytes,
+        },
+    }
+    detail = {}
+    for extra in [x for x in args.also.split(",") if x and x != name]:
+        del step
+        torch.cuda.empty_cache()
+        c2, step, ms2, k2, k2min, _ = run_workload(extra, dev, args.steps, args.warmup, args.kernel)
+        b2 = decode_bytes(c2)
+        detail[extra] = {"ms_per_step": round(ms2, 4),
+                         "GBps_step": round((b2 + cache_write_bytes(c2)) / (ms2 * 1e-3) / 1e9, 2),
+                         "decode_kernel_ms": round(k2, 4),
+                         "decode_kernel_GBps": round(b2 / (k2 * 1e-3) / 1e9, 2),
+                         "seq_heads_per_s": round(c2.spec.num_seqs * c2.spec.num_heads / (ms2 * 1e-3), 1),
+                         "kernel": chosen_kernel(c2, args.kernel)}
+        del c2
+    if detail:
+        rec["detail"] = detail
+    if snaps is not None:
+        rec["cpu_baseline"] = cpu_baseline(case, snaps, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

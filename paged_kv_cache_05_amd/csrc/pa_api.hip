@@ -1,0 +1,280 @@
+// C ABI of libpa: argument checks, launch planning and dispatch.  Everything here runs on
+// the host from host scalars only: no device memory is read, nothing synchronises, nothing
+// is allocated.  Declarations and the contract of every entry point are in include/pa.h.
+#include <cmath>
+#include <cstddef>
+
+#include "pa_common.h"
+
+namespace {
+
+using pa::DT;
+
+constexpr int32_t kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kDefaultPartition = 512;   // tokens per split-KV partition
+constexpr int kMinPartition = 128;
+constexpr long kTargetWorkgroups = 2048; // 256 CUs x 8 resident 4-wave workgroups
+
+bool dtype_of(pa_dtype d, DT* out) {
+  switch (d) {
+    case PA_F32: *out = DT::F32; return true;
+    case PA_F16: *out = DT::F16; return true;
+    case PA_BF16: *out = DT::BF16; return true;
+  }
+  return false;
+}
+int elem_bytes(DT d) { return d == DT::F32 ? 4 : 2; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plan {
+  int partition = 0;     // tokens per partition
+  int max_parts = 1;
+  size_t ws_ml_bytes = 0;
+  size_t ws_bytes = 0;   // total workspace (0: single pass)
+};
+
+// Shape checks shared by every decode entry point.
+pa_status check_shape(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_t maxb,
+                      int32_t partition_size) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || maxb <= 0 || partition_size < 0) return PA_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return PA_ERR_BAD_SHAPE;
+  if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
+  if (BS != 16 && BS != 32) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && partition_size % BS != 0) return PA_ERR_BAD_SHAPE;
+  if ((long)maxb * BS > (1L << 30)) return PA_ERR_BAD_SHAPE;
+  return PA_OK;
+}
+
+int auto_partition(int32_t S, int32_t Hq, int32_t BS, int32_t maxb) {
+  const long cap = (long)maxb * BS;
+  if (cap <= kDefaultPartition) return 0;  // one pass
+  int P = kDefaultPartition;
+  const long units = (long)S * Hq;
+  while (P > kMinPartition && units * ((cap + P - 1) / P) < kTargetWorkgroups) P /= 2;
+  return P;
+}
+
+Plan make_plan(int32_t S, int32_t Hq, int32_t D, int32_t BS, int32_t maxb, int32_t partition_size) {
+  Plan pl;
+  const long cap = (long)maxb * BS;
+  int P = partition_size > 0 ? partition_size : auto_partition(S, Hq, BS, maxb);
+  if (P == 0 || P >= cap) {
+    pl.partition = (int)((cap + 31) / 32 * 32);   // a single partition covers the table
+    pl.max_parts = 1;
+    return pl;
+  }
+  pl.partition = P;
+  pl.max_parts = (int)((cap + P - 1) / P);
+  const size_t units = (size_t)S * Hq * pl.max_parts;
+  pl.ws_ml_bytes = align256(units * 2 * sizeof(float));
+  pl.ws_bytes = pl.ws_ml_bytes + align256(units * D * sizeof(float));
+  return pl;
+}
+
+bool mfma_eligible(DT dt, int D, int G, int partition) {
+  return (dt == DT::F16 || dt == DT::BF16) && D == 128 && G % 4 == 0 && partition % 32 == 0;
+}
+
+int heads_per_wg(bool mfma, int G) {
+  if (mfma) return G % 16 == 0 ? 16 : G % 8 == 0 ? 8 : 4;
+  return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+}
+
+pa_status launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL_PTR: return "PA_ERR_NULL_PTR: a required pointer is NULL";
+    case PA_ERR_BAD_SHAPE: return "PA_ERR_BAD_SHAPE: a size is invalid or inconsistent";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported head_dim, block_size, dtype or kernel";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+  }
+  return "unknown pa_status";
+}
+
+int32_t pa_version(void) { return kVersion; }
+
+int32_t pa_decode_auto_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq) {
+  if (check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, 0) != PA_OK)
+    return 0;
+  return make_plan(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, 0).partition;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int32_t partition_size) {
+  if (check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                  partition_size) != PA_OK)
+    return 0;
+  return make_plan(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq, partition_size)
+      .ws_bytes;
+}
+
+pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                               pa_dtype dtype, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, pa_kernel kernel, void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, partition_size);
+  if (st != PA_OK) return st;
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_PTR;
+  if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+
+  const Plan pl = make_plan(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq,
+                            partition_size);
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return PA_ERR_WORKSPACE;
+
+  const int G = num_heads / num_kv_heads;
+  const bool can_mfma = mfma_eligible(dt, head_dim, G, pl.partition);
+  bool mfma = false;
+  if (kernel == PA_KERNEL_MFMA) {
+    if (!can_mfma) return PA_ERR_UNSUPPORTED;
+    mfma = true;
+  } else if (kernel == PA_KERNEL_AUTO) {
+    mfma = can_mfma;
+  }
+  const int gt = heads_per_wg(mfma, G);
+
+  pa::DecodeParams p;
+  p.out = out;
+  p.q = query;
+  p.kc = key_cache;
+  p.vc = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.ws_ml = pl.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
+  p.ws_o = pl.ws_bytes ? reinterpret_cast<float*>((char*)workspace + pl.ws_ml_bytes) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = G;
+  p.head_chunks = G / gt;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.partition = pl.partition;
+  p.max_parts = pl.max_parts;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  const long grid = (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts;
+  if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const hipError_t e = mfma ? pa::launch_decode_mfma(dt, head_dim, block_size, gt, p, (int)grid, s)
+                            : pa::launch_decode_valu(dt, head_dim, block_size, gt, p, (int)grid, s);
+  return launch_status(e);
+}
+
+pa_status pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype,
+                          int32_t partition_size, const void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, partition_size);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  const Plan pl = make_plan(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq,
+                            partition_size);
+  if (pl.max_parts <= 1) return PA_OK;   // nothing was split
+  if (!out || !context_lens) return PA_ERR_NULL_PTR;
+  if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+  pa::MergeParams p;
+  p.out = out;
+  p.context_lens = context_lens;
+  p.ws_ml = reinterpret_cast<const float*>(workspace);
+  p.ws_o = reinterpret_cast<const float*>((const char*)workspace + pl.ws_ml_bytes);
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.block_size = block_size;
+  p.partition = pl.partition;
+  p.max_parts = pl.max_parts;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_merge(dt, head_dim, p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode_ex(void* out, const void* query, const void* key_cache,
+                       const void* value_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                       pa_dtype dtype, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, pa_kernel kernel, void* stream) {
+  pa_status st = pa_decode_partitions(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                      block_size, num_blocks, max_blocks_per_seq, scale, dtype,
+                                      partition_size, workspace, workspace_bytes, kernel, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_merge(out, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                         block_size, max_blocks_per_seq, dtype, partition_size, workspace,
+                         workspace_bytes, stream);
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, pa_dtype dtype,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return pa_decode_ex(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, scale, dtype, partition_size, workspace,
+                      workspace_bytes, PA_KERNEL_AUTO, stream);
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype dtype, void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  const long row_bytes = (long)head_dim * elem_bytes(dt);
+  if (row_bytes % 16 != 0 || head_dim > 1024) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_reshape_and_cache(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens, (int)(row_bytes / 16),
+      block_size, num_blocks, num_kv_heads, reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  const long block_bytes = (long)num_kv_heads * block_size * head_dim * elem_bytes(dt);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_mapping) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
+                                              block_bytes / 16, num_blocks,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// KV-cache writers: reshape_and_cache (store each new token at its slot) and copy_blocks
+// (copy-on-write of whole blocks).  Both are pure data movement in 16-byte vectors; bits are
+// copied unchanged.
+//
+// reshape_and_cache: each decode step appends the new token's K/V to the cache
+// (PyTorch-CUDA-v2.9 PagedAttention page (jsqmd.com), paged-memory section and serving
+// workflow).  Token i goes to block slot/bs, offset slot%bs, every KV head.
+// copy_blocks: shared blocks are reference-counted and copied before a write (UltraLAB
+// summary of Kwon et al. (xasun.com) §一 and §二, sharing item).
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+// One workgroup per token; threads stride over the token's num_kv_heads * row_vecs vectors.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ kc,
+    uint4* __restrict__ vc, const int64_t* __restrict__ slots, int row_vecs, int block_size,
+    int64_t num_slots, int num_kv_heads) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;   // padding, or out of the pool
+  const int64_t b = slot / block_size;
+  const int off = (int)(slot - b * block_size);
+  const int total = num_kv_heads * row_vecs;
+  const uint4* ks = key + (size_t)i * total;
+  const uint4* vs = value + (size_t)i * total;
+  for (int v = threadIdx.x; v < total; v += blockDim.x) {
+    const int h = v / row_vecs, j = v - h * row_vecs;
+    const size_t dst = ((size_t)(b * num_kv_heads + h) * block_size + off) * row_vecs + j;
+    kc[dst] = ks[v];
+    vc[dst] = vs[v];
+  }
+}
+
+constexpr int kCopyUnroll = 4;
+constexpr int kCopyVecsPerWg = 256 * kCopyUnroll;
+
+// grid.x = pairs * 2 (K, V) * chunks; each workgroup copies up to 16 KiB of one block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc,
+                                                          uint4* __restrict__ vc,
+                                                          const int64_t* __restrict__ mapping,
+                                                          int64_t block_vecs, int chunks,
+                                                          int num_blocks) {
+  const int chunk = blockIdx.x % chunks;
+  const int which = (blockIdx.x / chunks) & 1;
+  const int pair = blockIdx.x / (2 * chunks);
+  const int64_t src = mapping[2 * pair], dst = mapping[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint4* pool = which ? vc : kc;
+  const uint4* s = pool + src * block_vecs;
+  uint4* d = pool + dst * block_vecs;
+  const int64_t v0 = (int64_t)chunk * kCopyVecsPerWg + threadIdx.x;
+  uint4 r[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t v = v0 + u * 256;
+    if (v < block_vecs) r[u] = s[v];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t v = v0 + u * 256;
+    if (v < block_vecs) d[v] = r[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
+                                    const int64_t* slots, int num_tokens, int row_vecs,
+                                    int block_size, int num_blocks, int num_kv_heads,
+                                    hipStream_t st) {
+  if (num_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(num_tokens), dim3(256), 0, st,
+                     (const uint4*)key, (const uint4*)value, (uint4*)kc, (uint4*)vc, slots,
+                     row_vecs, block_size, (int64_t)num_blocks * block_size, num_kv_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* kc, void* vc, const int64_t* mapping, int num_pairs,
+                              int64_t block_vecs, int num_blocks, hipStream_t st) {
+  if (num_pairs <= 0) return hipSuccess;
+  const int chunks = (int)((block_vecs + kCopyVecsPerWg - 1) / kCopyVecsPerWg);
+  const int64_t grid = (int64_t)num_pairs * 2 * chunks;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, st, (uint4*)kc,
+                     (uint4*)vc, mapping, block_vecs, chunks, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

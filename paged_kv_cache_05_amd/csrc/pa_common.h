@@ -1,0 +1,176 @@
+// Shared device helpers and internal launcher declarations for libpa (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------------
+// Element types.  Every kernel moves data in 16-byte vectors (one global_load_dwordx4 per
+// lane) and computes in fp32.
+// ---------------------------------------------------------------------------------------
+enum class DT { F32, F16, BF16 };
+
+template <DT> struct Elem;
+
+template <> struct Elem<DT::F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;
+  __device__ __forceinline__ static void unpack(const uint4 v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32: nearest-even
+}
+
+template <> struct Elem<DT::F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  __device__ __forceinline__ static void unpack(const uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16_lo(w[i]);
+      f[2 * i + 1] = f16_hi(w[i]);
+    }
+  }
+  __device__ __forceinline__ static uint4 pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f16_bits(f[2 * i]) | (f16_bits(f[2 * i + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// bfloat16 is the top half of an fp32 bit pattern.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN stays a quiet NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;          // round to nearest, ties to even
+}
+
+template <> struct Elem<DT::BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  __device__ __forceinline__ static void unpack(const uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ __forceinline__ static uint4 pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_bits(f[2 * i]) | (bf16_bits(f[2 * i + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// Cross-lane reductions inside groups of N consecutive lanes (N = 1, 8, 16, 32).  Every step
+// pairs each lane with one partner and adds (or maxes) the two values; since a + b and b + a
+// round identically, all lanes of a group end with the same bits.
+// ---------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8-lane half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16-lane row
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Softmax running state uses base-2 exponents: scores are pre-multiplied by log2(e).
+// A running max of -inf means "no token seen"; exp2(x - safe(m)) is then 0 for every x
+// that is itself -inf and the state stays empty.
+__device__ __forceinline__ float safe_max(float m) { return m == -INFINITY ? 0.0f : m; }
+
+// ---------------------------------------------------------------------------------------
+// Launch parameters shared by the decode kernels (all sizes validated on the host).
+// ---------------------------------------------------------------------------------------
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_ml;   // [S][Hq][max_parts][2] (running max in log2 units, denominator)
+  float* ws_o;    // [S][Hq][max_parts][D] normalised partial outputs
+  int32_t num_seqs, num_heads, num_kv_heads, group;   // group = num_heads / num_kv_heads
+  int32_t head_chunks;       // query-head chunks per KV head handled by separate workgroups
+  int32_t max_blocks_per_seq, num_blocks;
+  int32_t partition;         // tokens per partition (multiple of 16)
+  int32_t max_parts;         // partitions a full table can hold
+  float scale_log2;          // scale * log2(e)
+};
+
+struct MergeParams {
+  void* out;
+  const int32_t* context_lens;
+  const float* ws_ml;
+  const float* ws_o;
+  int32_t num_seqs, num_heads, max_blocks_per_seq, block_size, partition, max_parts;
+};
+
+// host-side launchers (return hipSuccess or the launch error)
+hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
+                              const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
+                              const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_merge(DT dt, int head_dim, const MergeParams& p, hipStream_t st);
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
+                                    const int64_t* slots, int num_tokens, int row_vecs,
+                                    int block_size, int num_blocks, int num_kv_heads,
+                                    hipStream_t st);
+hipError_t launch_copy_blocks(void* kc, void* vc, const int64_t* mapping, int num_pairs,
+                              int64_t block_vecs, int num_blocks, hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,325 @@
+// Paged decode attention for grouped-query attention on the matrix cores (gfx950).
+//
+// When G query heads share one KV head (the pages note that GQA/MQA shrinks the per-token KV
+// cache: UltraLAB summary of Kwon et al. (xasun.com), boundary note after §八), the G queries
+// against one K/V tile form two small dense products, S = Q K^T and O += P V.  They run on
+// v_mfma_f32_16x16x32_{bf16,f16}; the decode stays bound by HBM (about 4 flop per KV byte at
+// G = 4), and the matrix cores take the multiply-adds off the vector ALUs.
+//
+// Tiling.  A wave consumes 32 tokens per step (two 16-token chunks).
+//   Scores: S^T[16 tokens x 16 cols] = K_tile[16 x 128] * Q^T[128 x 16] (4 MFMAs per chunk).
+//     Column n holds query head n mod GT (heads are replicated when GT < 16).  A operand
+//     (K): lane l holds K[token l%16][32kc + 8(l/16) .. +8]; B operand (Q^T): lane l holds
+//     Q[head (l%16) mod GT][same 8 dims].  Output lane l, register i: score of token
+//     4(l/16)+i for head (l%16) mod GT.
+//   Output: O[16 rows x 16 cols] += P[16 x 32 tokens] * V[32 tokens x 16 cols], 8 column
+//     groups e = 0..7 with column n meaning dim 8n + e.  The k index 8(l/16)+j of lane l is
+//     token T(l/16, j) = 16(j/4) + 4(l/16) + j%4 -- exactly the tokens whose scores the lane
+//     already holds, so P needs no cross-lane movement.  The B operand (V) needs 8 tokens of
+//     one column per lane: lane l loads dims 8(l%16)..+8 of its 8 tokens (each load
+//     instruction reads 4 whole 256-byte rows) and transposes the 8x8 16-bit tile in
+//     registers with v_perm_b32.
+//   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group),
+//   so the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
+// Softmax state: running max per head (shared by all lanes holding that head, via two
+// cross-row shuffles per step); the output accumulators are rescaled only when some head's
+// max grows.  Partitions, wave interleaving and the final merge are as in the VALU kernel.
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <DT dt> struct Mfma;
+template <> struct Mfma<DT::BF16> {
+  __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
+  __device__ __forceinline__ static float value(uint32_t b) { return __uint_as_float(b << 16); }
+};
+template <> struct Mfma<DT::F16> {
+  __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
+  __device__ __forceinline__ static float value(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  }
+};
+
+// Column e (0..7) of an 8x8 tile of 16-bit values held as 8 rows r[j] (row j = token j,
+// word q = dims 2q, 2q+1): returns the 8 tokens' values of dim e, two per word.
+__device__ __forceinline__ uint4 tile_column(const uint4 (&r)[8], int e) {
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  auto word = [&](const uint4& v) -> uint32_t {
+    const int q = e >> 1;
+    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+  };
+  return make_uint4(__builtin_amdgcn_perm(word(r[1]), word(r[0]), sel),
+                    __builtin_amdgcn_perm(word(r[3]), word(r[2]), sel),
+                    __builtin_amdgcn_perm(word(r[5]), word(r[4]), sel),
+                    __builtin_amdgcn_perm(word(r[7]), word(r[6]), sel));
+}
+
+template <DT dt, int BS, int GT>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
+  constexpr int D = 128;
+  constexpr int EB = 2;            // element bytes
+  constexpr int ROW = D * EB;      // 256-byte token row
+  constexpr int CPB = BS / 16;
+  using M = Mfma<dt>;
+  static_assert(GT == 4 || GT == 8 || GT == 16, "heads per workgroup");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
+  const int lr = lane & 15, kg = lane >> 4;
+
+  int bid = blockIdx.x;
+  const int part = bid % p.max_parts;
+  bid /= p.max_parts;
+  const int hc = bid % (p.num_kv_heads * p.head_chunks);
+  const int s = bid / (p.num_kv_heads * p.head_chunks);
+  const int g = hc / p.head_chunks;
+  const int h0 = g * p.group + (hc % p.head_chunks) * GT;
+
+  int n = p.context_lens[s];
+  n = min(n, p.max_blocks_per_seq * BS);
+  const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
+  if (part >= nparts) return;
+  const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
+  if (n <= 0) {
+    if (threadIdx.x < GT * 16)
+      *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
+          make_uint4(0, 0, 0, 0);
+    return;
+  }
+
+  // Q^T operand (unscaled 16-bit values): lane l, chunk kc holds Q[h][32kc + 8kg .. +8]
+  uint4 qb[4];
+  {
+    const char* qp = (const char*)p.q + (q_row0 + (size_t)(lr % GT) * D) * EB;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
+  }
+
+  float m_run = -INFINITY;  // running max (log2 units) of head lr % GT
+  float l_run = 0.0f;       // this lane's share of that head's denominator
+  f32x4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int t_end = min(n, (part + 1) * p.partition);
+  const int u_begin = part * (p.partition / 32);
+  const int u_end = (t_end + 31) / 32;
+  const int ch_end = (t_end + 15) / 16;
+  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const size_t head_off = (size_t)g * BS * D;
+  const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
+  const int k_off = (lr * D + 8 * kg) * EB;   // K operand: token lr, dims 8kg.. (+32kc)
+  const int v_off = (4 * kg * D + 8 * lr) * EB;  // V rows: token 4kg (+j%4), dims 8lr..
+
+  auto tile_ptr = [&](const void* base, int phys, int ch) -> const char* {
+    return (const char*)base +
+           ((size_t)phys * block_stride + head_off + (size_t)(ch % CPB) * 16 * D) * EB;
+  };
+  auto load_unit = [&](uint4 (&kb)[8], uint4 (&vb)[8], int ph0, int ph1, int u) {
+    const char* k0 = tile_ptr(p.kc, ph0, 2 * u) + k_off;
+    const char* k1 = tile_ptr(p.kc, ph1, 2 * u + 1) + k_off;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      kb[kc] = *reinterpret_cast<const uint4*>(k0 + 64 * kc);
+      kb[4 + kc] = *reinterpret_cast<const uint4*>(k1 + 64 * kc);
+    }
+    const char* v0 = tile_ptr(p.vc, ph0, 2 * u) + v_off;
+    const char* v1 = tile_ptr(p.vc, ph1, 2 * u + 1) + v_off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vb[j] = *reinterpret_cast<const uint4*>(v0 + j * ROW);
+      vb[4 + j] = *reinterpret_cast<const uint4*>(v1 + j * ROW);
+    }
+  };
+  auto consume = [&](const uint4 (&kb)[8], uint4 (&vb)[8], int u, bool ok0, bool ok1) {
+    f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      st0 = M::mma(kb[kc], qb[kc], st0);
+      st1 = M::mma(kb[4 + kc], qb[kc], st1);
+    }
+    const int tok_base = 32 * u + 4 * kg;  // token of register j is tok_base + 16(j/4) + j%4
+    const bool full = ok0 && ok1 && (32 * u + 32 <= t_end);
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = st0[i] * p.scale_log2;
+      sv[4 + i] = st1[i] * p.scale_log2;
+    }
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool valid = (j < 4 ? ok0 : ok1) && (tok_base + 16 * (j / 4) + (j % 4) < t_end);
+        sv[j] = valid ? sv[j] : -INFINITY;
+        if (!valid) vb[j] = make_uint4(0, 0, 0, 0);   // masked rows may hold NaN
+      }
+    }
+    float bm = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sv[j]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m_run, bm);
+    const float ms = safe_max(mn);
+    if (__any(mn != m_run)) {
+      const float alpha = fast_exp2(m_run - ms);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, (kg * 4 + i) % GT);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e][i] *= a;
+      }
+    }
+    m_run = mn;
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = fast_exp2(sv[j] - ms);
+      l_run += pj;
+      hi[j] = M::bits(pj);
+      lo[j] = M::bits(pj - M::value(hi[j]));
+    }
+    const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                 hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+    const uint4 plo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                 lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint4 bv = tile_column(vb, e);
+      acc[e] = M::mma(phi, bv, acc[e]);
+      acc[e] = M::mma(plo, bv, acc[e]);
+    }
+  };
+
+  // units of this wave: u_begin + wave + 4*i; table entries of both chunks, one unit per lane
+  for (int base = u_begin + wave; base < u_end; base += 4 * kWave) {
+    const int cnt = min(kWave, (u_end - base + 3) / 4);
+    int e0 = -1, e1 = -1;
+    if (lane < cnt) {
+      const int c0 = 2 * (base + 4 * lane);
+      if (c0 < ch_end) e0 = table[c0 / CPB];
+      if (c0 + 1 < ch_end) e1 = table[(c0 + 1) / CPB];
+    }
+    auto phys = [&](int ent, int i, bool& ok) {
+      const int b = __builtin_amdgcn_readlane(ent, i);
+      ok = (unsigned)b < (unsigned)p.num_blocks;  // unused or bad ids read block 0, masked
+      return ok ? b : 0;
+    };
+    // Two register buffers, steady-state loads unconditional (see the vector-ALU kernel).
+    uint4 ka[8], va[8], kb2[8], vb2[8];
+    bool a0, a1, b0, b1;
+    auto load_i = [&](uint4 (&kb)[8], uint4 (&vb)[8], int i, bool& o0, bool& o1) {
+      const int x0 = phys(e0, i, o0), x1 = phys(e1, i, o1);
+      load_unit(kb, vb, x0, x1, base + 4 * i);
+    };
+    load_i(ka, va, 0, a0, a1);
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+      load_i(kb2, vb2, i + 1, b0, b1);
+      consume(ka, va, base + 4 * i, a0, a1);
+      load_i(ka, va, i + 2, a0, a1);
+      consume(kb2, vb2, base + 4 * (i + 1), b0, b1);
+    }
+    if (i + 1 < cnt) {
+      load_i(kb2, vb2, i + 1, b0, b1);
+      consume(ka, va, base + 4 * i, a0, a1);
+      consume(kb2, vb2, base + 4 * (i + 1), b0, b1);
+    } else {
+      consume(ka, va, base + 4 * i, a0, a1);
+    }
+  }
+
+  // this wave's denominator per head: sum the four token groups
+  float lt = l_run + __shfl_xor(l_run, 16);
+  lt += __shfl_xor(lt, 32);
+
+  __shared__ float s_o[4][GT][D];
+  __shared__ float s_m[4][GT], s_l[4][GT];
+  if (kg * 4 < GT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][kg * 4 + i][8 * lr + e] = acc[e][i];
+  }
+  if (lane < GT) {
+    s_m[wave][lane] = m_run;
+    s_l[wave][lane] = lt;
+  }
+  __syncthreads();
+  if (threadIdx.x < GT * 16) {
+    const int h = threadIdx.x / 16, cc = threadIdx.x % 16;
+    float Mx = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+    const float ms = safe_max(Mx);
+    float L = 0.0f, O[8] = {};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // waves hold unnormalised sums relative to their own max: rescale both to M
+      const float wt = fast_exp2(s_m[w][h] - ms);
+      L = fmaf(wt, s_l[w][h], L);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[e] = fmaf(wt, s_o[w][h][cc * 8 + e], O[e]);
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[e] *= inv;
+    const size_t qrow = q_row0 + (size_t)h * D;
+    if (nparts == 1) {
+      *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * 8) * EB) = Elem<dt>::pack(O);
+    } else {
+      const size_t slot = (size_t)(s * p.num_heads + h0 + h) * p.max_parts + part;
+      float* po = p.ws_o + slot * D + cc * 8;
+      *reinterpret_cast<float4*>(po) = make_float4(O[0], O[1], O[2], O[3]);
+      *reinterpret_cast<float4*>(po + 4) = make_float4(O[4], O[5], O[6], O[7]);
+      if (cc == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(Mx, L);
+    }
+  }
+}
+
+template <DT dt, int BS>
+hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  switch (gt) {
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 4>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 8>), dim3(grid), dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 16>), dim3(grid), dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <DT dt>
+hipError_t launch_bs(int bs, int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  if (bs == 16) return launch_gt<dt, 16>(gt, p, grid, st);
+  if (bs == 32) return launch_gt<dt, 32>(gt, p, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
+                              const DecodeParams& p, int grid, hipStream_t st) {
+  if (head_dim != 128) return hipErrorInvalidValue;
+  switch (dt) {
+    case DT::F16: return launch_bs<DT::F16>(block_size, heads_per_wg, p, grid, st);
+    case DT::BF16: return launch_bs<DT::BF16>(block_size, heads_per_wg, p, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

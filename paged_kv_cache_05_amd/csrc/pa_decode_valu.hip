@@ -1,0 +1,306 @@
+// Paged decode attention on the vector ALUs (gfx950, wave64).
+//
+// What is computed: for one query per (sequence, head), softmax-weighted sum of V over the
+// sequence's cached tokens, with K/V fetched block by block through the block table (UltraLAB
+// summary of Kwon et al. (xasun.com) §二, attention-algorithm item; scaled dot-product
+// attention, "PagedAttention技术：加速GPT推理的利器" (yunthe.com) §1.1).
+//
+// Work decomposition.  One workgroup (4 waves) per (sequence, KV head, query-head chunk,
+// partition of P tokens).  Splitting one sequence over partitions is what lets long contexts
+// spread over all 256 CUs; the partial results are merged exactly by their log-sum-exp
+// weights (pa_merge.hip).  A partition is cut into 16-token chunks; wave w takes chunks w,
+// w+4, w+8, ...
+//
+// Data path for one chunk.  A (block, KV head) tile is block_size * head_dim contiguous
+// elements.  One 16-byte load per lane moves 1 KiB per wave: with LPT = head_dim*elem/16 lanes
+// per token row, a wave covers TPI = 64/LPT consecutive tokens per load instruction, fully
+// coalesced.  Scores are reduced over the LPT lanes of a row with DPP; each row of lanes keeps
+// its own online-softmax state (running max, denominator, partial output), so the loop has no
+// cross-row traffic.  Rows and waves are merged once, at the end of the partition.
+// The next chunk's K and V loads are issued before the current chunk is consumed.
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+template <DT dt, int D, int BS, int GT>
+struct ValuCfg {
+  using E = Elem<dt>;
+  static constexpr int EPL = E::kPerVec;     // elements per lane per 16-byte vector
+  static constexpr int LPT = D / EPL;        // lanes per token row
+  static constexpr int TPI = kWave / LPT;    // tokens per wave load instruction
+  static constexpr int NI = 16 / TPI;        // load instructions per 16-token chunk
+  static constexpr int CPB = BS / 16;        // chunks per block
+  static constexpr int ROW_BYTES = D * E::kBytes;
+  static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row must span 8..32 lanes");
+  static_assert(BS % 16 == 0, "block size must be a multiple of 16");
+};
+
+template <DT dt, int D, int BS, int GT>
+__global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) {
+  using C = ValuCfg<dt, D, BS, GT>;
+  using E = typename C::E;
+  constexpr int EPL = C::EPL, LPT = C::LPT, TPI = C::TPI, NI = C::NI, CPB = C::CPB;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
+  const int row = lane / LPT;   // token slot inside one load instruction
+  const int col = lane % LPT;   // 16-byte column of the token row
+
+  int bid = blockIdx.x;
+  const int part = bid % p.max_parts;
+  bid /= p.max_parts;
+  const int hc = bid % (p.num_kv_heads * p.head_chunks);
+  const int s = bid / (p.num_kv_heads * p.head_chunks);
+  const int g = hc / p.head_chunks;
+  const int h0 = g * p.group + (hc % p.head_chunks) * GT;
+
+  int n = p.context_lens[s];
+  n = min(n, p.max_blocks_per_seq * BS);
+  const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
+  if (part >= nparts) return;
+
+  const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
+  if (n <= 0) {  // empty context: the output is defined as zero
+    if (wave == 0 && row == 0) {
+      const float z[EPL] = {};
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+        *reinterpret_cast<uint4*>((char*)p.out + (q_row0 + (size_t)h * D + col * EPL) * E::kBytes) =
+            E::pack(z);
+    }
+    return;
+  }
+
+  // query, pre-scaled by scale*log2(e), as fp32
+  float qf[GT][EPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const uint4 v = *reinterpret_cast<const uint4*>((const char*)p.q +
+                                                    (q_row0 + (size_t)h * D + col * EPL) * E::kBytes);
+    E::unpack(v, qf[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[h][e] *= p.scale_log2;
+  }
+
+  float m[GT], l[GT], o[GT][EPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
+  }
+
+  const int t_end = min(n, (part + 1) * p.partition);
+  const int ch_begin = part * (p.partition / 16);
+  const int ch_end = (t_end + 15) / 16;
+  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const size_t head_off = (size_t)g * BS * D;               // elements
+  const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
+  const int lane_off = (row * D + col * EPL) * E::kBytes;    // bytes inside a 16-token chunk
+
+  // address of this lane's first vector of chunk `ch` (physical block `phys`)
+  auto chunk_ptr = [&](const void* base, int phys, int ch) -> const char* {
+    const size_t el = (size_t)phys * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
+    return (const char*)base + el * E::kBytes + lane_off;
+  };
+  auto load_chunk = [&](uint4 (&kb)[NI], uint4 (&vb)[NI], int phys, int ch) {
+    const char* kp = chunk_ptr(p.kc, phys, ch);
+    const char* vp = chunk_ptr(p.vc, phys, ch);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kb[i] = *reinterpret_cast<const uint4*>(kp + i * TPI * C::ROW_BYTES);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vb[i] = *reinterpret_cast<const uint4*>(vp + i * TPI * C::ROW_BYTES);
+  };
+  auto consume = [&](const uint4 (&kb)[NI], const uint4 (&vb)[NI], int ch, bool ok) {
+    const int tok0 = ch * 16 + row;
+    const bool full = ok && (ch * 16 + 16 <= t_end);
+    float sc[NI][GT];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float kf[EPL];
+      E::unpack(kb[i], kf);
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[h][e], kf[e], acc);
+        sc[i][h] = group_sum<LPT>(acc);
+      }
+      if (!full) {
+        const bool valid = ok && (tok0 + i * TPI < t_end);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) sc[i][h] = valid ? sc[i][h] : -INFINITY;
+      }
+    }
+    float pr[NI][GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float bm = sc[0][h];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) bm = fmaxf(bm, sc[i][h]);
+      const float mn = fmaxf(m[h], bm);
+      const float ms = safe_max(mn);
+      const float alpha = fast_exp2(m[h] - ms);
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        pr[i][h] = fast_exp2(sc[i][h] - ms);
+        ps += pr[i][h];
+      }
+      l[h] = l[h] * alpha + ps;
+      m[h] = mn;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPL];
+      E::unpack(vb[i], vf);
+      if (!full) {
+        const bool valid = ok && (tok0 + i * TPI < t_end);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = valid ? vf[e] : 0.0f;  // masked slots may hold NaN
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr[i][h], vf[e], o[h][e]);
+    }
+  };
+
+  // chunks of this wave: ch_begin + wave + 4*i; their table entries are fetched 64 at a time,
+  // one per lane, and broadcast with readlane
+  for (int base = ch_begin + wave; base < ch_end; base += 4 * kWave) {
+    const int cnt = min(kWave, (ch_end - base + 3) / 4);
+    int ent = 0;
+    {
+      const int my_ch = base + 4 * lane;
+      if (lane < cnt) ent = table[my_ch / CPB];
+    }
+    auto phys_of = [&](int i, bool& ok) {
+      int b = __builtin_amdgcn_readlane(ent, i);
+      ok = (unsigned)b < (unsigned)p.num_blocks;   // a bad id reads block 0 and is masked
+      return ok ? b : 0;
+    };
+    // Two register buffers; in the steady state every iteration issues the next chunk's
+    // loads unconditionally before consuming the current one, so the wait before a consume
+    // covers only the older chunk (a conditional load would force a wait for everything).
+    uint4 ka[NI], va[NI], kb[NI], vb[NI];
+    bool oka, okb;
+    load_chunk(ka, va, phys_of(0, oka), base);
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      consume(ka, va, base + 4 * i, oka);
+      load_chunk(ka, va, phys_of(i + 2, oka), base + 4 * (i + 2));
+      consume(kb, vb, base + 4 * (i + 1), okb);
+    }
+    if (i + 1 < cnt) {
+      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      consume(ka, va, base + 4 * i, oka);
+      consume(kb, vb, base + 4 * (i + 1), okb);
+    } else {
+      consume(ka, va, base + 4 * i, oka);
+    }
+  }
+
+  // merge the rows of each wave (xor-butterfly over lane groups)
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float mp = __shfl_xor(m[h], off);
+      const float lp = __shfl_xor(l[h], off);
+      const float mn = fmaxf(m[h], mp);
+      const float ms = safe_max(mn);
+      const float a0 = fast_exp2(m[h] - ms), a1 = fast_exp2(mp - ms);
+      l[h] = l[h] * a0 + lp * a1;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = o[h][e] * a0 + __shfl_xor(o[h][e], off) * a1;
+      m[h] = mn;
+    }
+  }
+
+  // merge the 4 waves through LDS
+  __shared__ float s_o[4][GT][D];
+  __shared__ float s_m[4][GT], s_l[4][GT];
+  if (row == 0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[wave][h][col * EPL + e] = o[h][e];
+      if (col == 0) {
+        s_m[wave][h] = m[h];
+        s_l[wave][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < GT * LPT) {
+    const int h = threadIdx.x / LPT, cc = threadIdx.x % LPT;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    const float ms = safe_max(M);
+    float L = 0.0f, O[EPL] = {};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // waves hold unnormalised sums relative to their own max: rescale both to M
+      const float wt = fast_exp2(s_m[w][h] - ms);
+      L = fmaf(wt, s_l[w][h], L);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) O[e] = fmaf(wt, s_o[w][h][cc * EPL + e], O[e]);
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[e] *= inv;
+    const size_t qrow = q_row0 + (size_t)h * D;
+    if (nparts == 1) {
+      *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * EPL) * E::kBytes) = E::pack(O);
+    } else {
+      const size_t slot = (size_t)(s * p.num_heads + h0 + h) * p.max_parts + part;
+      float* po = p.ws_o + slot * D + cc * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(po + e) = make_float4(O[e], O[e + 1], O[e + 2], O[e + 3]);
+      if (cc == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(M, L);
+    }
+  }
+}
+
+template <DT dt, int D, int BS>
+hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  switch (gt) {
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 1>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 2>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 4>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 8>), dim3(grid), dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <DT dt>
+hipError_t launch_dt(int d, int bs, int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  if (d == 64 && bs == 16) return launch_gt<dt, 64, 16>(gt, p, grid, st);
+  if (d == 64 && bs == 32) return launch_gt<dt, 64, 32>(gt, p, grid, st);
+  if (d == 128 && bs == 16) return launch_gt<dt, 128, 16>(gt, p, grid, st);
+  if (d == 128 && bs == 32) return launch_gt<dt, 128, 32>(gt, p, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
+                              const DecodeParams& p, int grid, hipStream_t st) {
+  switch (dt) {
+    case DT::F32: return launch_dt<DT::F32>(head_dim, block_size, heads_per_wg, p, grid, st);
+    case DT::F16: return launch_dt<DT::F16>(head_dim, block_size, heads_per_wg, p, grid, st);
+    case DT::BF16: return launch_dt<DT::BF16>(head_dim, block_size, heads_per_wg, p, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,219 @@
+"""Thin ctypes binding over libpa.so (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks their shapes and
+dtypes, and calls the C entry point of the same name on the current HIP stream.  All work runs
+in the library's kernels; nothing here computes.  If ``libpa.so`` has not been built, or a
+tensor is not on the GPU, the call raises -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpa.so")
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "pa.h"
+
+PA_OK = 0
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+_c_int, _c_size, _c_float, _p = ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+_SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [_c_int]),
+    "pa_version": (_c_int, []),
+    "pa_decode_auto_partition": (_c_int, [_c_int] * 6),
+    "pa_decode_workspace_bytes": (_c_size, [_c_int] * 7),
+    "pa_decode": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _p, _c_size, _p]),
+    "pa_decode_ex": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _p, _c_size,
+                                                          _c_int, _p]),
+    "pa_decode_partitions": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _p,
+                                                                  _c_size, _c_int, _p]),
+    "pa_decode_merge": (_c_int, [_p, _p] + [_c_int] * 8 + [_p, _c_size, _p]),
+    "pa_reshape_and_cache": (_c_int, [_p] * 5 + [_c_int] * 6 + [_p]),
+    "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
+}
+
+
+def header_symbols() -> list[str]:
+    """Every function include/pa.h declares."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(pa_\w+)\s*\(", text, re.M)))
+
+
+def load():
+    """Load libpa.so (once); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "paged_kv_cache_05_amd.build.build() (hipcc, gfx950)")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, f"{what}: {status_string(status)}")
+
+
+# ---------------------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported element type {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dev(*tensors):
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors are on different devices")
+    return dev
+
+
+def _stream(dev, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                    partition_size=0) -> int:
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                block_size, max_blocks_per_seq, partition_size))
+
+
+def auto_partition(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) -> int:
+    return int(load().pa_decode_auto_partition(num_seqs, num_heads, num_kv_heads, head_dim,
+                                               block_size, max_blocks_per_seq))
+
+
+def _decode_shapes(out, query, key_cache, value_cache, block_tables, context_lens):
+    import torch
+    S, Hq, D = query.shape
+    NB, Hkv, BS, D2 = key_cache.shape
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or D2 != D:
+        raise ValueError("key_cache/value_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must have the query's shape")
+    if not (out.dtype == query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("out, query and both pools must share one element type")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    return S, Hq, Hkv, D, BS, NB, block_tables.shape[1]
+
+
+def decode(out, query, key_cache, value_cache, block_tables, context_lens, scale, *,
+           partition_size=0, kernel="auto", workspace=None, stream=None):
+    """pa_decode_ex: paged decode attention into ``out`` ([S, Hq, d])."""
+    import torch
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    S, Hq, Hkv, D, BS, NB, maxb = _decode_shapes(out, query, key_cache, value_cache, block_tables,
+                                                 context_lens)
+    need = workspace_bytes(S, Hq, Hkv, D, BS, maxb, partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_ex(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                               _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS, NB, maxb,
+                               float(scale), _dtype_code(query), int(partition_size),
+                               _ptr(workspace), wsb, KERNELS[kernel], _stream(dev, stream)),
+           "pa_decode_ex")
+    return out
+
+
+def decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                      workspace, *, partition_size=0, kernel="auto", stream=None):
+    """pa_decode_partitions: the first of pa_decode's two launches."""
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    S, Hq, Hkv, D, BS, NB, maxb = _decode_shapes(out, query, key_cache, value_cache, block_tables,
+                                                 context_lens)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_partitions(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                       _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS,
+                                       NB, maxb, float(scale), _dtype_code(query),
+                                       int(partition_size), _ptr(workspace), wsb, KERNELS[kernel],
+                                       _stream(dev, stream)), "pa_decode_partitions")
+
+
+def decode_merge(out, context_lens, num_kv_heads, block_size, max_blocks_per_seq, workspace, *,
+                 partition_size=0, stream=None):
+    """pa_decode_merge: the second of pa_decode's two launches."""
+    dev = _dev(out, context_lens, workspace)
+    S, Hq, D = out.shape
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_merge(_ptr(out), _ptr(context_lens), S, Hq, num_kv_heads, D,
+                                  block_size, max_blocks_per_seq, _dtype_code(out),
+                                  int(partition_size), _ptr(workspace), wsb, _stream(dev, stream)),
+           "pa_decode_merge")
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, stream=None):
+    """pa_reshape_and_cache: store key/value [N, Hkv, d] at slot_mapping [N] (int64)."""
+    import torch
+    dev = _dev(key, value, key_cache, value_cache, slot_mapping)
+    N, Hkv, D = key.shape
+    NB, Hkv2, BS, D2 = key_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(value.shape) != tuple(key.shape) \
+            or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("shape mismatch between new tokens and the pools")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (N,):
+        raise TypeError("slot_mapping must be int64 [num_tokens]")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("key, value and both pools must share one element type")
+    _check(load().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                       _ptr(slot_mapping), N, Hkv, D, BS, NB, _dtype_code(key),
+                                       _stream(dev, stream)), "pa_reshape_and_cache")
+
+
+def copy_blocks(key_cache, value_cache, block_mapping, *, stream=None):
+    """pa_copy_blocks: copy whole blocks src -> dst for each row of block_mapping [P, 2] (int64)."""
+    import torch
+    dev = _dev(key_cache, value_cache, block_mapping)
+    NB, Hkv, BS, D = key_cache.shape
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or key_cache.dtype != value_cache.dtype:
+        raise ValueError("key_cache and value_cache must match")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [num_pairs, 2]")
+    _check(load().pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(block_mapping),
+                                 block_mapping.shape[0], Hkv, D, BS, NB, _dtype_code(key_cache),
+                                 _stream(dev, stream)), "pa_copy_blocks")

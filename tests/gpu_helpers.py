@@ -1,0 +1,127 @@
+"""Shared pieces of the GPU parity tests: uploading generated cases, running the library
+through its binding, the oracle side of a decode step, and the attention tolerance.
+
+Tolerance (for fp16/bf16 inputs with fp32 accumulation): against the float64 oracle rounded
+once (nearest-even) to the output type, max |err| <= 2e-3 * max|V| over the V entries the call
+reads, and ||err||_2 / ||ref||_2 <= 1e-3 over the whole output.  Rounding a correct result to
+bfloat16 alone already moves it by ~1.6e-3 in relative L2, so the comparison is made against
+the rounded oracle; the error against the unrounded oracle is reported, not gated.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_05_amd import ops
+from paged_kv_cache_05_amd import workloads as W
+
+MAX_ABS_FACTOR = 2e-3
+REL_L2_BOUND = 1e-3
+
+
+def need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Uploaded:
+    def __init__(self, case: W.DecodeCase, dev):
+        import torch
+        dt = case.dtype
+        self.case = case
+        self.q = W.to_torch(case.query, dt, dev)
+        if isinstance(case.key_cache, np.ndarray):
+            self.kc = W.to_torch(case.key_cache, dt, dev)
+            self.vc = W.to_torch(case.value_cache, dt, dev)
+        else:
+            self.kc, self.vc = case.key_cache, case.value_cache
+        self.bt = torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).to(dev)
+        self.cl = torch.from_numpy(np.ascontiguousarray(case.context_lens, np.int32)).to(dev)
+        self.nk = W.to_torch(case.new_key, dt, dev)
+        self.nv = W.to_torch(case.new_value, dt, dev)
+        self.slots = torch.from_numpy(np.ascontiguousarray(case.slot_mapping, np.int64)).to(dev)
+        self.pairs = torch.from_numpy(np.ascontiguousarray(case.block_mapping, np.int64).reshape(-1, 2)).to(dev)
+        self.out = torch.empty_like(self.q)
+
+    def decode(self, kernel="auto", partition_size=0):
+        import torch
+        ops.decode(self.out, self.q, self.kc, self.vc, self.bt, self.cl, float(self.case.scale),
+                   partition_size=partition_size, kernel=kernel)
+        torch.cuda.synchronize()
+        return W.from_torch(self.out, self.case.dtype)
+
+    def step(self, kernel="auto", partition_size=0):
+        """copy_blocks -> reshape_and_cache -> decode on one stream."""
+        if len(self.case.block_mapping):
+            ops.copy_blocks(self.kc, self.vc, self.pairs)
+        if len(self.case.slot_mapping):
+            ops.reshape_and_cache(self.nk, self.nv, self.kc, self.vc, self.slots)
+        return self.decode(kernel, partition_size)
+
+
+def oracle_decode(case: W.DecodeCase, key_cache=None, value_cache=None, context_lens=None):
+    return oracle.decode_ref(case.query, case.key_cache if key_cache is None else key_cache,
+                             case.value_cache if value_cache is None else value_cache,
+                             case.block_tables,
+                             case.context_lens if context_lens is None else context_lens,
+                             case.block_size, case.scale, case.dtype)
+
+
+def oracle_step(case: W.DecodeCase):
+    """Oracle for copy_blocks -> reshape_and_cache -> decode on a host-generated case."""
+    kc, vc = case.key_cache, case.value_cache
+    if len(case.block_mapping):
+        kc, vc = oracle.copy_blocks_ref(kc, vc, case.block_mapping)
+    if len(case.slot_mapping):
+        kc, vc = oracle.reshape_and_cache_ref(case.new_key, case.new_value, kc, vc,
+                                              case.slot_mapping, case.block_size)
+    return oracle_decode(case, kc, vc), kc, vc
+
+
+def live_vmax(case: W.DecodeCase, value_cache=None) -> float:
+    vc = case.value_cache if value_cache is None else value_cache
+    m = 0.0
+    for s in range(case.spec.num_seqs):
+        n = int(case.context_lens[s])
+        if n > 0:
+            V = oracle.resolve_sequence(vc, case.block_tables[s], n, case.block_size, case.dtype)
+            m = max(m, float(np.max(np.abs(V))))
+    return m
+
+
+def attention_errors(gpu_storage, ref64, dtype):
+    ref_r = oracle.storage_to_f64(oracle.f64_to_storage(ref64, dtype), dtype)
+    got = oracle.storage_to_f64(gpu_storage, dtype)
+    err = got - ref_r
+    max_abs = float(np.max(np.abs(err))) if err.size else 0.0
+    denom = float(np.linalg.norm(ref_r))
+    rel = float(np.linalg.norm(err)) / denom if denom > 0 else float(np.linalg.norm(err))
+    rel_unrounded = float(np.linalg.norm(got - ref64)) / max(float(np.linalg.norm(ref64)), 1e-300)
+    return max_abs, rel, rel_unrounded
+
+
+def assert_attention_close(gpu_storage, ref64, dtype, vmax, what=""):
+    got = oracle.storage_to_f64(gpu_storage, dtype)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    max_abs, rel, rel_u = attention_errors(gpu_storage, ref64, dtype)
+    tol = MAX_ABS_FACTOR * vmax
+    say(f"  {what}: max_abs={max_abs:.3e} (tol {tol:.3e}) rel_l2={rel:.3e} (tol {REL_L2_BOUND}) "
+        f"rel_l2_vs_unrounded={rel_u:.3e}")
+    assert max_abs <= tol, f"{what}: max abs error {max_abs} > {tol}"
+    assert rel <= REL_L2_BOUND, f"{what}: relative L2 error {rel} > {REL_L2_BOUND}"
+    return max_abs, rel
+
+
+def bits(storage, dtype):
+    a = np.ascontiguousarray(storage)
+    return a.view(np.uint32) if dtype == "f32" else a.view(np.uint16)

@@ -1,0 +1,103 @@
+"""The C-ABI library: it loads, exports every symbol include/pa.h declares, and rejects bad
+arguments with the documented status codes before launching anything (no GPU needed: every
+call here returns during host-side validation)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from paged_kv_cache_05_amd import ops
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not ops.LIB_PATH.exists():
+        from paged_kv_cache_05_amd.build import build
+        build()
+    return ops.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = ops.header_symbols()
+    assert len(declared) >= 10
+    nm = subprocess.run(["nm", "-D", "--defined-only", str(ops.LIB_PATH)], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert getattr(lib, s) is not None
+
+
+def test_status_strings_and_version(lib):
+    for code in range(6):
+        s = ops.status_string(code)
+        assert s.startswith("PA_")
+    assert lib.pa_version() >= 10000
+
+
+def _decode(lib, **kw):
+    a = dict(out=1, q=1, kc=1, vc=1, bt=1, cl=1, S=4, Hq=8, Hkv=2, D=128, BS=16, NB=100, maxb=8,
+             scale=0.1, dtype=2, P=0, ws=None, wsb=0, kernel=0)
+    a.update(kw)
+    p = lambda v: ctypes.c_void_p(v) if v else None
+    return lib.pa_decode_ex(p(a["out"]), p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), p(a["cl"]),
+                            a["S"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"], a["maxb"],
+                            a["scale"], a["dtype"], a["P"], p(a["ws"]), a["wsb"], a["kernel"], None)
+
+
+def test_decode_argument_errors(lib):
+    assert _decode(lib, out=0) == 1                  # PA_ERR_NULL_PTR
+    assert _decode(lib, bt=0) == 1
+    assert _decode(lib, Hq=6, Hkv=4) == 2            # PA_ERR_BAD_SHAPE: heads not a multiple
+    assert _decode(lib, S=-1) == 2
+    assert _decode(lib, maxb=0) == 2
+    assert _decode(lib, NB=0) == 2
+    assert _decode(lib, P=24) == 2                   # not a multiple of block_size
+    assert _decode(lib, scale=float("nan")) == 2
+    assert _decode(lib, D=96) == 3                   # PA_ERR_UNSUPPORTED
+    assert _decode(lib, BS=8) == 3
+    assert _decode(lib, dtype=7) == 3
+    assert _decode(lib, kernel=9) == 3
+    assert _decode(lib, kernel=2, dtype=0) == 3      # matrix-core path needs f16/bf16
+    assert _decode(lib, kernel=2, Hq=6, Hkv=3) == 3  # group of 2
+    assert _decode(lib, kernel=2, D=64) == 3
+    assert _decode(lib, maxb=64, P=64) == 4          # split needs a workspace
+    assert _decode(lib, maxb=64, P=64, ws=1, wsb=16) == 4
+    assert _decode(lib, S=0, out=0, q=0) == 0        # empty batch: no-op
+
+
+def test_workspace_and_partition_sizes(lib):
+    # one pass when the table fits one partition: no workspace
+    assert ops.workspace_bytes(4, 2, 2, 64, 16, 7) == 0
+    # 256 seqs x 32 heads x 8 partitions x (2 + 128) floats, each region 256-byte aligned
+    assert ops.workspace_bytes(256, 32, 32, 128, 16, 256, 512) == 256 * 32 * 8 * 2 * 4 + 256 * 32 * 8 * 128 * 4
+    assert ops.auto_partition(256, 32, 32, 128, 16, 256) == 512
+    # few heads -> smaller partitions so the grid still fills the GPU
+    assert ops.auto_partition(1, 8, 8, 128, 16, 2048) < 512
+    assert ops.auto_partition(4, 2, 2, 64, 16, 7) >= 7 * 16
+    # 112-token table in 48-token partitions: 3 partitions -> 256 B (ml) + 6144 B (o)
+    assert ops.workspace_bytes(4, 2, 2, 64, 16, 7, 48) == 256 + 4 * 2 * 3 * 64 * 4
+    assert ops.workspace_bytes(4, 2, 2, 96, 16, 7) == 0    # unsupported -> 0
+
+
+def test_cache_kernel_argument_errors(lib):
+    p = ctypes.c_void_p(1)
+    assert lib.pa_reshape_and_cache(None, p, p, p, p, 4, 2, 64, 16, 64, 0, None) == 1
+    assert lib.pa_reshape_and_cache(p, p, p, p, p, -1, 2, 64, 16, 64, 0, None) == 2
+    assert lib.pa_reshape_and_cache(p, p, p, p, p, 4, 2, 3, 16, 64, 1, None) == 3   # 6-byte rows
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 2, 64, 16, 64, 0, None) == 0
+    assert lib.pa_copy_blocks(p, p, None, 3, 2, 64, 16, 64, 0, None) == 1
+    assert lib.pa_copy_blocks(p, p, p, -2, 2, 64, 16, 64, 0, None) == 2
+    assert lib.pa_copy_blocks(p, p, p, 1, 2, 64, 16, 64, 5, None) == 3
+    assert lib.pa_copy_blocks(None, None, None, 0, 2, 64, 16, 64, 0, None) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(2, 2, 64)
+    kc = torch.zeros(4, 2, 16, 64)
+    with pytest.raises(ValueError):
+        ops.decode(x, x, kc, kc, torch.zeros(2, 1, dtype=torch.int32),
+                   torch.ones(2, dtype=torch.int32), 0.125)

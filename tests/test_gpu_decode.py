@@ -1,0 +1,150 @@
+"""GPU parity: pa_decode (both kernel families, split and single pass) against the float64
+oracle on seeded inputs small enough for the oracle, spanning several chunks, partitions and a
+ragged tail; plus bit-level invariants (determinism, placement permutation, one-token
+contexts, poisoned unused memory)."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (Uploaded, assert_attention_close, bits, live_vmax, need_gpu,
+                         oracle_decode, say)
+from paged_kv_cache_05_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+# lengths around block, chunk and partition edges, plus a long one
+EDGE_LENGTHS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1000]
+
+
+def _case(dtype, D, BS, Hq, Hkv, lengths=EDGE_LENGTHS, seed=100, **kw):
+    kw.setdefault("new_tokens", ("free", 0))
+    spec = W.CaseSpec(f"t_{dtype}_{D}_{BS}_{Hq}_{Hkv}", seed, len(lengths), Hq, Hkv, D, dtype, BS,
+                      ("fixed", list(lengths)), **kw)
+    return W.build_case(spec)
+
+
+def _mfma_ok(dtype, D, Hq, Hkv, P):
+    return dtype in ("f16", "bf16") and D == 128 and (Hq // Hkv) % 4 == 0 and P % 32 == 0
+
+
+@pytest.mark.parametrize("partition", [0, 64, 48])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_decode_matches_oracle(dtype, D, BS, kernel, partition):
+    dev = need_gpu()
+    Hq, Hkv = 8, 2
+    if partition % BS:
+        pytest.skip("partition must be a multiple of the block size")
+    if kernel == "mfma" and not _mfma_ok(dtype, D, Hq, Hkv, partition or 512):
+        pytest.skip("matrix-core kernel needs f16/bf16, head_dim 128, groups of 4k")
+    say(f"decode {dtype} D={D} BS={BS} kernel={kernel} P={partition}")
+    c = _case(dtype, D, BS, Hq, Hkv, seed=zlib.crc32(f"{dtype}{D}{BS}".encode()) % 1000)
+    u = Uploaded(c, dev)
+    got = u.decode(kernel, partition)
+    ref = oracle_decode(c)
+    assert_attention_close(got, ref, dtype, live_vmax(c), f"{dtype}/{D}/{BS}/{kernel}/P{partition}")
+
+
+@pytest.mark.parametrize("heads", [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1)])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_head_groupings(heads, kernel):
+    dev = need_gpu()
+    Hq, Hkv = heads
+    if kernel == "mfma" and not _mfma_ok("bf16", 128, Hq, Hkv, 64):
+        pytest.skip("group not a multiple of 4")
+    say(f"groups Hq={Hq} Hkv={Hkv} kernel={kernel}")
+    c = _case("bf16", 128, 16, Hq, Hkv, lengths=[1, 17, 100, 333, 700], seed=7)
+    u = Uploaded(c, dev)
+    for P in (0, 64):
+        got = u.decode(kernel, P)
+        assert_attention_close(got, oracle_decode(c), "bf16", live_vmax(c), f"G={Hq // Hkv}/{kernel}/P{P}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_peaky_softmax(dtype, kernel):
+    """q x 30: scores spread over ~100 units; needs the running max."""
+    dev = need_gpu()
+    c = _case(dtype, 128, 16, 8, 2, lengths=[5, 300, 1000], seed=11, q_scale=30.0)
+    u = Uploaded(c, dev)
+    for P in (0, 64):
+        assert_attention_close(u.decode(kernel, P), oracle_decode(c), dtype, live_vmax(c),
+                               f"peaky/{dtype}/{kernel}/P{P}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_token_is_exact(dtype, kernel):
+    """A one-token context returns that token's V bit for bit."""
+    dev = need_gpu()
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("no f32 matrix-core path")
+    c = _case(dtype, 128, 16, 8, 2, lengths=[1] * 5, seed=12)
+    got = Uploaded(c, dev).decode(kernel)
+    ref = oracle_decode(c)
+    assert np.array_equal(bits(got, dtype), bits(W.round_to_storage(ref.astype(np.float32), dtype), dtype))
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_deterministic_and_placement_invariant(kernel):
+    """Same inputs -> same bits; moving blocks to other physical ids (table rewritten) -> same
+    bits, because the arithmetic order depends only on logical positions."""
+    dev = need_gpu()
+    c = _case("bf16", 128, 16, 8, 2, lengths=[3, 40, 129, 600, 1000], seed=13)
+    u = Uploaded(c, dev)
+    for P in (0, 64):
+        a = u.decode(kernel, P)
+        b = u.decode(kernel, P)
+        assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
+        pi = np.random.default_rng(1).permutation(c.num_blocks)
+        c2 = W.build_case(c.spec)
+        c2.key_cache = np.empty_like(c.key_cache)
+        c2.value_cache = np.empty_like(c.value_cache)
+        c2.key_cache[pi] = c.key_cache
+        c2.value_cache[pi] = c.value_cache
+        c2.block_tables = np.where(c.block_tables >= 0, pi[np.clip(c.block_tables, 0, None)],
+                                   c.block_tables).astype(np.int32)
+        d = Uploaded(c2, dev).decode(kernel, P)
+        assert np.array_equal(bits(a, "bf16"), bits(d, "bf16"))
+
+
+@pytest.mark.parametrize("fill", [-1, 2**31 - 1])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_poisoned_unused_memory(kernel, fill):
+    """NaN in every slot no sequence reads and junk in unused table entries: same bits as the
+    clean run, all finite."""
+    dev = need_gpu()
+    spec = W.CaseSpec("poison", 14, 6, 8, 2, 128, "bf16", 16, ("fixed", [1, 15, 16, 17, 300, 513]),
+                      new_tokens=("free", 0), max_blocks_per_seq=40)
+    clean = W.build_case(spec)
+    dirty = W.build_case(spec, poison=True, table_fill=fill)
+    for P in (0, 64):
+        a = Uploaded(clean, dev).decode(kernel, P)
+        b = Uploaded(dirty, dev).decode(kernel, P)
+        assert np.all(np.isfinite(oracle.storage_to_f64(b, "bf16")))
+        assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_empty_context_gives_zero(kernel):
+    dev = need_gpu()
+    c = _case("f16", 128, 16, 8, 2, lengths=[0, 5, 0, 70], seed=15)
+    got = Uploaded(c, dev).decode(kernel)
+    ref = oracle_decode(c)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert_attention_close(got, ref, "f16", live_vmax(c), "empty-context")
+
+
+def test_split_and_single_pass_agree():
+    dev = need_gpu()
+    c = _case("bf16", 128, 32, 32, 32, lengths=[2000, 4096, 1, 777], seed=16)
+    u = Uploaded(c, dev)
+    ref = oracle_decode(c)
+    vmax = live_vmax(c)
+    for P in (32, 64, 512, 4096):
+        assert_attention_close(u.decode("valu", P), ref, "bf16", vmax, f"P={P}")
