@@ -127,6 +127,14 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Streaming 16-byte load: K/V tiles are read exactly once per call, so they are fetched with
+// the non-temporal hint and do not displace reusable lines in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* ptr) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Softmax running state uses base-2 exponents: scores are pre-multiplied by log2(e).
 // A running max of -inf means "no token seen"; exp2(x - safe(m)) is then 0 for every x
 // that is itself -inf and the state stays empty.

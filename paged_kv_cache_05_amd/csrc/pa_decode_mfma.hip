@@ -80,26 +80,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int lr = lane & 15, kg = lane >> 4;
 
-  int bid = blockIdx.x;
-  const int part = bid % p.max_parts;
-  bid /= p.max_parts;
-  const int hc = bid % (p.num_kv_heads * p.head_chunks);
-  const int s = bid / (p.num_kv_heads * p.head_chunks);
+  // Workgroups are dealt round-robin to the 8 XCDs (id mod 8).  The partition index is the
+  // slowest grid index so every XCD gets an even share of (sequence, head) units; with it
+  // fastest, XCD k would receive only partition k.
+  const int units = p.num_seqs * p.num_kv_heads * p.head_chunks;
+  const int part = blockIdx.x / units;
+  const int unit = blockIdx.x - part * units;
+  const int hc = unit % (p.num_kv_heads * p.head_chunks);
+  const int s = unit / (p.num_kv_heads * p.head_chunks);
   const int g = hc / p.head_chunks;
   const int h0 = g * p.group + (hc % p.head_chunks) * GT;
 
-  int n = p.context_lens[s];
-  n = min(n, p.max_blocks_per_seq * BS);
-  const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
-  if (part >= nparts) return;
+  // Loads independent of the context length first (their latency overlaps the read of
+  // context_lens): the Q^T operand and the table entries of this wave's first 64 units.
   const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
-  if (n <= 0) {
-    if (threadIdx.x < GT * 16)
-      *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
-          make_uint4(0, 0, 0, 0);
-    return;
-  }
-
+  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int u_begin = part * (p.partition / 32);
   // Q^T operand (unscaled 16-bit values): lane l, chunk kc holds Q[h][32kc + 8kg .. +8]
   uint4 qb[4];
   {
@@ -107,6 +103,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
       qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
+  }
+  int e0_first = -1, e1_first = -1;
+  {
+    const int cap = p.max_blocks_per_seq * CPB;   // chunks the table row can address
+    const int c0 = 2 * (u_begin + wave + 4 * lane);
+    if (c0 < cap) e0_first = table[c0 / CPB];
+    if (c0 + 1 < cap) e1_first = table[(c0 + 1) / CPB];
+  }
+
+  int n = p.context_lens[s];
+  n = min(n, p.max_blocks_per_seq * BS);
+  const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
+  if (part >= nparts) return;
+  if (n <= 0) {
+    if (threadIdx.x < GT * 16)
+      *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
+          make_uint4(0, 0, 0, 0);
+    return;
   }
 
   float m_run = -INFINITY;  // running max (log2 units) of head lr % GT
@@ -116,10 +130,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int t_end = min(n, (part + 1) * p.partition);
-  const int u_begin = part * (p.partition / 32);
   const int u_end = (t_end + 31) / 32;
   const int ch_end = (t_end + 15) / 16;
-  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const size_t head_off = (size_t)g * BS * D;
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
   const int k_off = (lr * D + 8 * kg) * EB;   // K operand: token lr, dims 8kg.. (+32kc)
@@ -134,15 +146,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     const char* k1 = tile_ptr(p.kc, ph1, 2 * u + 1) + k_off;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      kb[kc] = *reinterpret_cast<const uint4*>(k0 + 64 * kc);
-      kb[4 + kc] = *reinterpret_cast<const uint4*>(k1 + 64 * kc);
+      kb[kc] = load_stream(k0 + 64 * kc);
+      kb[4 + kc] = load_stream(k1 + 64 * kc);
     }
     const char* v0 = tile_ptr(p.vc, ph0, 2 * u) + v_off;
     const char* v1 = tile_ptr(p.vc, ph1, 2 * u + 1) + v_off;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      vb[j] = *reinterpret_cast<const uint4*>(v0 + j * ROW);
-      vb[4 + j] = *reinterpret_cast<const uint4*>(v1 + j * ROW);
+      vb[j] = load_stream(v0 + j * ROW);
+      vb[4 + j] = load_stream(v1 + j * ROW);
     }
   };
   auto consume = [&](const uint4 (&kb)[8], uint4 (&vb)[8], int u, bool ok0, bool ok1) {
@@ -209,11 +221,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   // units of this wave: u_begin + wave + 4*i; table entries of both chunks, one unit per lane
   for (int base = u_begin + wave; base < u_end; base += 4 * kWave) {
     const int cnt = min(kWave, (u_end - base + 3) / 4);
-    int e0 = -1, e1 = -1;
-    if (lane < cnt) {
-      const int c0 = 2 * (base + 4 * lane);
-      if (c0 < ch_end) e0 = table[c0 / CPB];
-      if (c0 + 1 < ch_end) e1 = table[(c0 + 1) / CPB];
+    // A chunk past the context (second half of a ragged last unit) may carry any id here:
+    // ids outside the pool read block 0, and every token of such a chunk is masked.
+    int e0 = e0_first, e1 = e1_first;
+    if (base != u_begin + wave) {
+      e0 = e1 = -1;
+      if (lane < cnt) {
+        const int c0 = 2 * (base + 4 * lane);
+        if (c0 < ch_end) e0 = table[c0 / CPB];
+        if (c0 + 1 < ch_end) e1 = table[(c0 + 1) / CPB];
+      }
     }
     auto phys = [&](int ent, int i, bool& ok) {
       const int b = __builtin_amdgcn_readlane(ent, i);

@@ -47,20 +47,39 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int row = lane / LPT;   // token slot inside one load instruction
   const int col = lane % LPT;   // 16-byte column of the token row
 
-  int bid = blockIdx.x;
-  const int part = bid % p.max_parts;
-  bid /= p.max_parts;
-  const int hc = bid % (p.num_kv_heads * p.head_chunks);
-  const int s = bid / (p.num_kv_heads * p.head_chunks);
+  // Workgroups are dealt round-robin to the 8 XCDs (id mod 8).  The partition index is the
+  // slowest grid index so every XCD gets an even share of (sequence, head) units; with it
+  // fastest, XCD k would receive only partition k.
+  const int units = p.num_seqs * p.num_kv_heads * p.head_chunks;
+  const int part = blockIdx.x / units;
+  const int unit = blockIdx.x - part * units;
+  const int hc = unit % (p.num_kv_heads * p.head_chunks);
+  const int s = unit / (p.num_kv_heads * p.head_chunks);
   const int g = hc / p.head_chunks;
   const int h0 = g * p.group + (hc % p.head_chunks) * GT;
+
+  // Loads that do not depend on the context length go first, so their latency overlaps the
+  // read of context_lens: the query rows and the table entries of this wave's first chunks
+  // (entries past the sequence's end are loaded but never used; all lie inside the table row).
+  const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
+  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int ch_begin = part * (p.partition / 16);
+  uint4 qraw[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h)
+    qraw[h] = *reinterpret_cast<const uint4*>((const char*)p.q +
+                                              (q_row0 + (size_t)h * D + col * EPL) * E::kBytes);
+  int ent_first = -1;
+  {
+    const int my_ch = ch_begin + wave + 4 * lane;
+    if (my_ch < p.max_blocks_per_seq * CPB) ent_first = table[my_ch / CPB];
+  }
 
   int n = p.context_lens[s];
   n = min(n, p.max_blocks_per_seq * BS);
   const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
   if (part >= nparts) return;
 
-  const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
   if (n <= 0) {  // empty context: the output is defined as zero
     if (wave == 0 && row == 0) {
       const float z[EPL] = {};
@@ -76,9 +95,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   float qf[GT][EPL];
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4*>((const char*)p.q +
-                                                    (q_row0 + (size_t)h * D + col * EPL) * E::kBytes);
-    E::unpack(v, qf[h]);
+    E::unpack(qraw[h], qf[h]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[h][e] *= p.scale_log2;
   }
@@ -93,9 +110,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
 
   const int t_end = min(n, (part + 1) * p.partition);
-  const int ch_begin = part * (p.partition / 16);
   const int ch_end = (t_end + 15) / 16;
-  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const size_t head_off = (size_t)g * BS * D;               // elements
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
   const int lane_off = (row * D + col * EPL) * E::kBytes;    // bytes inside a 16-token chunk
@@ -109,9 +124,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     const char* kp = chunk_ptr(p.kc, phys, ch);
     const char* vp = chunk_ptr(p.vc, phys, ch);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kb[i] = *reinterpret_cast<const uint4*>(kp + i * TPI * C::ROW_BYTES);
+    for (int i = 0; i < NI; ++i) kb[i] = load_stream(kp + i * TPI * C::ROW_BYTES);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vb[i] = *reinterpret_cast<const uint4*>(vp + i * TPI * C::ROW_BYTES);
+    for (int i = 0; i < NI; ++i) vb[i] = load_stream(vp + i * TPI * C::ROW_BYTES);
   };
   auto consume = [&](const uint4 (&kb)[NI], const uint4 (&vb)[NI], int ch, bool ok) {
     const int tok0 = ch * 16 + row;
@@ -171,13 +186,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   };
 
   // chunks of this wave: ch_begin + wave + 4*i; their table entries are fetched 64 at a time,
-  // one per lane, and broadcast with readlane
+  // one per lane, and broadcast with readlane (the first 64 were fetched above)
   for (int base = ch_begin + wave; base < ch_end; base += 4 * kWave) {
     const int cnt = min(kWave, (ch_end - base + 3) / 4);
-    int ent = 0;
-    {
+    int ent = ent_first;
+    if (base != ch_begin + wave) {
       const int my_ch = base + 4 * lane;
-      if (lane < cnt) ent = table[my_ch / CPB];
+      ent = lane < cnt ? table[my_ch / CPB] : -1;
     }
     auto phys_of = [&](int i, bool& ok) {
       int b = __builtin_amdgcn_readlane(ent, i);

@@ -73,9 +73,11 @@ def test_workspace_and_partition_sizes(lib):
     assert ops.workspace_bytes(4, 2, 2, 64, 16, 7) == 0
     # 256 seqs x 32 heads x 8 partitions x (2 + 128) floats, each region 256-byte aligned
     assert ops.workspace_bytes(256, 32, 32, 128, 16, 256, 512) == 256 * 32 * 8 * 2 * 4 + 256 * 32 * 8 * 128 * 4
-    assert ops.auto_partition(256, 32, 32, 128, 16, 256) == 512
-    # few heads -> smaller partitions so the grid still fills the GPU
-    assert ops.auto_partition(1, 8, 8, 128, 16, 2048) < 512
+    # many (sequence, KV head) units: long partitions, capped at 2048 tokens
+    assert ops.auto_partition(256, 32, 32, 128, 16, 256) == 2048
+    # few units -> smaller partitions so the grid still fills the GPU (floor 256)
+    assert ops.auto_partition(1, 8, 8, 128, 16, 2048) == 256
+    assert ops.auto_partition(16, 32, 8, 128, 16, 2048) == 2048
     assert ops.auto_partition(4, 2, 2, 64, 16, 7) >= 7 * 16
     # 112-token table in 48-token partitions: 3 partitions -> 256 B (ml) + 6144 B (o)
     assert ops.workspace_bytes(4, 2, 2, 64, 16, 7, 48) == 256 + 4 * 2 * 3 * 64 * 4
