@@ -96,6 +96,7 @@ class Step:
         self.pairs = torch.from_numpy(case.block_mapping.reshape(-1, 2)).to(dev)
         self.out = torch.empty_like(self.q)
         self.P = sp.partition_size
+        self.shared = bool(sp.shared_prefix)   # blocks read by several sequences of the call
         nbytes = ops.workspace_bytes(sp.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim,
                                      sp.block_size, case.max_blocks_per_seq, self.P)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -108,7 +109,7 @@ class Step:
             ev[0].record()
         ops.decode_partitions(self.out, self.q, self.kc, self.vc, self.bt, self.cl,
                               float(self.case.scale), self.ws, partition_size=self.P,
-                              kernel=self.kernel)
+                              kernel=self.kernel, shared_blocks=self.shared)
         if ev is not None:
             ev[1].record()
         ops.decode_merge(self.out, self.cl, self.case.spec.num_kv_heads, self.case.spec.block_size,
@@ -234,7 +235,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
-    ap.add_argument("--also", default="llama7b_bs32",
+    ap.add_argument("--also", default="llama7b_bs32,opt13b,gqa_long,shared_prefix",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -58,6 +58,16 @@ typedef enum {
   PA_KERNEL_MFMA = 2   /* matrix-core kernel for grouped-query attention (f16/bf16) */
 } pa_kernel;
 
+/*
+ * Flags for pa_decode_ex / pa_decode_partitions (bitwise OR; 0 is what pa_decode uses).
+ * PA_DECODE_SHARED_BLOCKS: some physical blocks are read by several sequences of this call
+ * (a shared prompt prefix, parallel-sampling siblings; xasun.com summary §二, sharing item).
+ * K/V are then fetched with cache-allocating loads so later readers of a shared block hit in
+ * the L2; without the flag they are fetched as streaming (non-temporal) loads, which is faster
+ * when every block is read once.  The results are identical either way.
+ */
+#define PA_DECODE_SHARED_BLOCKS 0x1u
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pa_status_string(pa_status s);
 
@@ -122,10 +132,11 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_decode_ex — pa_decode with an explicit kernel family.  PA_KERNEL_MFMA requires
- * dtype f16/bf16 and num_heads / num_kv_heads in {4, 8, 16} (PA_ERR_UNSUPPORTED otherwise);
- * PA_KERNEL_VALU accepts every supported shape.  Same arguments, results and errors as
- * pa_decode otherwise.
+ * pa_decode_ex — pa_decode with an explicit kernel family and flags.  PA_KERNEL_MFMA
+ * requires dtype f16/bf16, head_dim 128 and num_heads / num_kv_heads a multiple of 4
+ * (PA_ERR_UNSUPPORTED otherwise); PA_KERNEL_VALU accepts every supported shape.  `flags` is
+ * a combination of PA_DECODE_* bits (unknown bits: PA_ERR_UNSUPPORTED).  Same arguments,
+ * results and errors as pa_decode otherwise.
  */
 pa_status pa_decode_ex(void* out, const void* query, const void* key_cache,
                        const void* value_cache, const int32_t* block_tables,
@@ -133,7 +144,7 @@ pa_status pa_decode_ex(void* out, const void* query, const void* key_cache,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
                        pa_dtype dtype, int32_t partition_size, void* workspace,
-                       size_t workspace_bytes, pa_kernel kernel, void* stream);
+                       size_t workspace_bytes, pa_kernel kernel, uint32_t flags, void* stream);
 
 /*
  * The two launches of pa_decode, exposed so a caller (or a profiler harness) can bracket
@@ -149,7 +160,8 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
                                pa_dtype dtype, int32_t partition_size, void* workspace,
-                               size_t workspace_bytes, pa_kernel kernel, void* stream);
+                               size_t workspace_bytes, pa_kernel kernel, uint32_t flags,
+                               void* stream);
 
 pa_status pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs,
                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

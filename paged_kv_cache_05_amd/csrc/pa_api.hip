@@ -81,7 +81,7 @@ Plan make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_
 }
 
 bool mfma_eligible(DT dt, int D, int G, int partition) {
-  return (dt == DT::F16 || dt == DT::BF16) && D == 128 && G % 4 == 0 && partition % 32 == 0;
+  return (dt == DT::F16 || dt == DT::BF16) && D == 128 && G % 4 == 0 && partition % 16 == 0;
 }
 
 int heads_per_wg(bool mfma, int G) {
@@ -133,7 +133,8 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
                                pa_dtype dtype, int32_t partition_size, void* workspace,
-                               size_t workspace_bytes, pa_kernel kernel, void* stream) {
+                               size_t workspace_bytes, pa_kernel kernel, uint32_t flags,
+                               void* stream) {
   DT dt;
   if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
   pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -141,6 +142,7 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   if (st != PA_OK) return st;
   if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
     return PA_ERR_UNSUPPORTED;
+  if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
@@ -186,8 +188,9 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const hipError_t e = mfma ? pa::launch_decode_mfma(dt, head_dim, block_size, gt, p, (int)grid, s)
-                            : pa::launch_decode_valu(dt, head_dim, block_size, gt, p, (int)grid, s);
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
+  const hipError_t e = mfma ? pa::launch_decode_mfma(dt, head_dim, block_size, gt, stream_kv, p, (int)grid, s)
+                            : pa::launch_decode_valu(dt, head_dim, block_size, gt, stream_kv, p, (int)grid, s);
   return launch_status(e);
 }
 
@@ -228,11 +231,12 @@ pa_status pa_decode_ex(void* out, const void* query, const void* key_cache,
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
                        pa_dtype dtype, int32_t partition_size, void* workspace,
-                       size_t workspace_bytes, pa_kernel kernel, void* stream) {
+                       size_t workspace_bytes, pa_kernel kernel, uint32_t flags, void* stream) {
   pa_status st = pa_decode_partitions(out, query, key_cache, value_cache, block_tables,
                                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                                       block_size, num_blocks, max_blocks_per_seq, scale, dtype,
-                                      partition_size, workspace, workspace_bytes, kernel, stream);
+                                      partition_size, workspace, workspace_bytes, kernel, flags,
+                                      stream);
   if (st != PA_OK) return st;
   return pa_decode_merge(out, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                          block_size, max_blocks_per_seq, dtype, partition_size, workspace,
@@ -248,7 +252,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
   return pa_decode_ex(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
                       num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_blocks_per_seq, scale, dtype, partition_size, workspace,
-                      workspace_bytes, PA_KERNEL_AUTO, stream);
+                      workspace_bytes, PA_KERNEL_AUTO, 0u, stream);
 }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,

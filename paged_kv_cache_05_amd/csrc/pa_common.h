@@ -135,6 +135,14 @@ __device__ __forceinline__ uint4 load_stream(const void* ptr) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// K/V tile load: streaming by default; an ordinary (cache-allocating) load when the caller
+// says blocks are shared by several sequences of the call, so later readers hit in L2.
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_kv(const void* ptr) {
+  if constexpr (STREAM) return load_stream(ptr);
+  else return *reinterpret_cast<const uint4*>(ptr);
+}
+
 // Softmax running state uses base-2 exponents: scores are pre-multiplied by log2(e).
 // A running max of -inf means "no token seen"; exp2(x - safe(m)) is then 0 for every x
 // that is itself -inf and the state stays empty.
@@ -170,9 +178,9 @@ struct MergeParams {
 
 // host-side launchers (return hipSuccess or the launch error)
 hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
-                              const DecodeParams& p, int grid, hipStream_t st);
+                              bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
-                              const DecodeParams& p, int grid, hipStream_t st);
+                              bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_merge(DT dt, int head_dim, const MergeParams& p, hipStream_t st);
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int64_t* slots, int num_tokens, int row_vecs,

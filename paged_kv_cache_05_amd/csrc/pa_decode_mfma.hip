@@ -2,28 +2,28 @@
 //
 // When G query heads share one KV head (the pages note that GQA/MQA shrinks the per-token KV
 // cache: UltraLAB summary of Kwon et al. (xasun.com), boundary note after §八), the G queries
-// against one K/V tile form two small dense products, S = Q K^T and O += P V.  They run on
-// v_mfma_f32_16x16x32_{bf16,f16}; the decode stays bound by HBM (about 4 flop per KV byte at
-// G = 4), and the matrix cores take the multiply-adds off the vector ALUs.
+// against one K/V tile form two small dense products, S = Q K^T and O += P V.  They run on the
+// matrix cores; the decode stays bound by HBM (about 4 flop per KV byte at G = 4), and the
+// matrix cores take the multiply-adds off the vector ALUs.
 //
-// Tiling.  A wave consumes 32 tokens per step (two 16-token chunks).
-//   Scores: S^T[16 tokens x 16 cols] = K_tile[16 x 128] * Q^T[128 x 16] (4 MFMAs per chunk).
-//     Column n holds query head n mod GT (heads are replicated when GT < 16).  A operand
-//     (K): lane l holds K[token l%16][32kc + 8(l/16) .. +8]; B operand (Q^T): lane l holds
-//     Q[head (l%16) mod GT][same 8 dims].  Output lane l, register i: score of token
-//     4(l/16)+i for head (l%16) mod GT.
-//   Output: O[16 rows x 16 cols] += P[16 x 32 tokens] * V[32 tokens x 16 cols], 8 column
-//     groups e = 0..7 with column n meaning dim 8n + e.  The k index 8(l/16)+j of lane l is
-//     token T(l/16, j) = 16(j/4) + 4(l/16) + j%4 -- exactly the tokens whose scores the lane
-//     already holds, so P needs no cross-lane movement.  The B operand (V) needs 8 tokens of
-//     one column per lane: lane l loads dims 8(l%16)..+8 of its 8 tokens (each load
-//     instruction reads 4 whole 256-byte rows) and transposes the 8x8 16-bit tile in
-//     registers with v_perm_b32.
-//   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group),
-//   so the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
-// Softmax state: running max per head (shared by all lanes holding that head, via two
-// cross-row shuffles per step); the output accumulators are rescaled only when some head's
-// max grows.  Partitions, wave interleaving and the final merge are as in the VALU kernel.
+// Tiling.  A wave consumes one 16-token chunk (one block of 16, or half a block of 32) per step.
+//   Scores: S^T[16 tokens x 16 cols] = K_chunk[16 x 128] * Q^T[128 x 16], four
+//     v_mfma_f32_16x16x32 ops.  Column n holds query head n mod GT (heads are replicated when
+//     GT < 16).  A operand (K): lane l holds K[token l%16][32kc + 8(l/16) .. +8]; B operand
+//     (Q^T): lane l holds Q[head (l%16) mod GT][same 8 dims].  Result: lane l, register i holds
+//     the score of token 4(l/16)+i for head (l%16) mod GT.
+//   Output: O[16 rows x 16 cols] += P[16 x 16 tokens] * V[16 tokens x 16 cols], eight
+//     v_mfma_f32_16x16x16 ops per column group e = 0..7, column n meaning dim 8n + e.  The A
+//     operand (P) of lane l is head (l%16) mod GT at tokens 4(l/16) .. +4: exactly the four
+//     scores the lane already holds, so P never moves between lanes.  The B operand needs four
+//     tokens of one column per lane: lane l loads dims 8(l%16) .. +8 of tokens 4(l/16) .. +4
+//     (each load instruction reads four whole 256-byte rows) and transposes the 4x8 16-bit
+//     tile in registers with v_perm_b32.
+//   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group), so
+//   the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
+// Softmax state: running max per head, shared by the four lanes holding that head (two
+// cross-row shuffles per chunk); accumulators are rescaled only when some head's max grows.
+// Partitions, wave interleaving, prefetch and the final merge follow the vector-ALU kernel.
 #include "pa_common.h"
 
 namespace pa {
@@ -32,20 +32,30 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 template <DT dt> struct Mfma;
 template <> struct Mfma<DT::BF16> {
-  __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+  __device__ __forceinline__ static f32x4 mma32(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 mma16(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
   }
   __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
   __device__ __forceinline__ static float value(uint32_t b) { return __uint_as_float(b << 16); }
 };
 template <> struct Mfma<DT::F16> {
-  __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+  __device__ __forceinline__ static f32x4 mma32(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 mma16(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
   __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
   __device__ __forceinline__ static float value(uint32_t b) {
@@ -53,26 +63,24 @@ template <> struct Mfma<DT::F16> {
   }
 };
 
-// Column e (0..7) of an 8x8 tile of 16-bit values held as 8 rows r[j] (row j = token j,
-// word q = dims 2q, 2q+1): returns the 8 tokens' values of dim e, two per word.
-__device__ __forceinline__ uint4 tile_column(const uint4 (&r)[8], int e) {
+// Column e (0..7) of a 4x8 tile of 16-bit values held as 4 rows r[j] (row j = token j, word q
+// = dims 2q, 2q+1): the 4 tokens' values of dim e, two per word, token order preserved.
+__device__ __forceinline__ uint2 tile_column(const uint4 (&r)[4], int e) {
   const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
   auto word = [&](const uint4& v) -> uint32_t {
     const int q = e >> 1;
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
   };
-  return make_uint4(__builtin_amdgcn_perm(word(r[1]), word(r[0]), sel),
-                    __builtin_amdgcn_perm(word(r[3]), word(r[2]), sel),
-                    __builtin_amdgcn_perm(word(r[5]), word(r[4]), sel),
-                    __builtin_amdgcn_perm(word(r[7]), word(r[6]), sel));
+  return make_uint2(__builtin_amdgcn_perm(word(r[1]), word(r[0]), sel),
+                    __builtin_amdgcn_perm(word(r[3]), word(r[2]), sel));
 }
 
-template <DT dt, int BS, int GT>
+template <DT dt, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int D = 128;
   constexpr int EB = 2;            // element bytes
   constexpr int ROW = D * EB;      // 256-byte token row
-  constexpr int CPB = BS / 16;
+  constexpr int CPB = BS / 16;     // 16-token chunks per block
   using M = Mfma<dt>;
   static_assert(GT == 4 || GT == 8 || GT == 16, "heads per workgroup");
 
@@ -80,9 +88,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int lr = lane & 15, kg = lane >> 4;
 
-  // Workgroups are dealt round-robin to the 8 XCDs (id mod 8).  The partition index is the
-  // slowest grid index so every XCD gets an even share of (sequence, head) units; with it
-  // fastest, XCD k would receive only partition k.
+  // Workgroups are dealt round-robin to the 8 XCDs (id mod 8); the partition index is the
+  // slowest grid index so every XCD gets an even share of (sequence, head) units.
   const int units = p.num_seqs * p.num_kv_heads * p.head_chunks;
   const int part = blockIdx.x / units;
   const int unit = blockIdx.x - part * units;
@@ -92,31 +99,29 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int h0 = g * p.group + (hc % p.head_chunks) * GT;
 
   // Loads independent of the context length first (their latency overlaps the read of
-  // context_lens): the Q^T operand and the table entries of this wave's first 64 units.
+  // context_lens): the Q^T operand and the table entries of this wave's first 64 chunks
+  // (entries past the sequence's end are loaded but never used; all lie inside the row).
   const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int u_begin = part * (p.partition / 32);
-  // Q^T operand (unscaled 16-bit values): lane l, chunk kc holds Q[h][32kc + 8kg .. +8]
-  uint4 qb[4];
+  const int ch_begin = part * (p.partition / 16);
+  uint4 qb[4];  // Q^T operand (unscaled 16-bit values): chunk kc holds Q[h][32kc + 8kg .. +8]
   {
     const char* qp = (const char*)p.q + (q_row0 + (size_t)(lr % GT) * D) * EB;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
       qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
   }
-  int e0_first = -1, e1_first = -1;
+  int ent_first = -1;
   {
-    const int cap = p.max_blocks_per_seq * CPB;   // chunks the table row can address
-    const int c0 = 2 * (u_begin + wave + 4 * lane);
-    if (c0 < cap) e0_first = table[c0 / CPB];
-    if (c0 + 1 < cap) e1_first = table[(c0 + 1) / CPB];
+    const int my_ch = ch_begin + wave + 4 * lane;
+    if (my_ch < p.max_blocks_per_seq * CPB) ent_first = table[my_ch / CPB];
   }
 
   int n = p.context_lens[s];
   n = min(n, p.max_blocks_per_seq * BS);
   const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
   if (part >= nparts) return;
-  if (n <= 0) {
+  if (n <= 0) {  // empty context: the output is defined as zero
     if (threadIdx.x < GT * 16)
       *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
           make_uint4(0, 0, 0, 0);
@@ -130,59 +135,39 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int t_end = min(n, (part + 1) * p.partition);
-  const int u_end = (t_end + 31) / 32;
   const int ch_end = (t_end + 15) / 16;
   const size_t head_off = (size_t)g * BS * D;
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
-  const int k_off = (lr * D + 8 * kg) * EB;   // K operand: token lr, dims 8kg.. (+32kc)
-  const int v_off = (4 * kg * D + 8 * lr) * EB;  // V rows: token 4kg (+j%4), dims 8lr..
+  const int k_off = (lr * D + 8 * kg) * EB;       // K operand: token lr, dims 8kg.. (+32kc)
+  const int v_off = (4 * kg * D + 8 * lr) * EB;   // V rows: token 4kg (+j), dims 8lr..
 
-  auto tile_ptr = [&](const void* base, int phys, int ch) -> const char* {
-    return (const char*)base +
-           ((size_t)phys * block_stride + head_off + (size_t)(ch % CPB) * 16 * D) * EB;
+  auto load_chunk = [&](uint4 (&kb)[4], uint4 (&vb)[4], int phys, int ch) {
+    const size_t el = (size_t)phys * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
+    const char* kp = (const char*)p.kc + el * EB + k_off;
+    const char* vp = (const char*)p.vc + el * EB + v_off;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) kb[kc] = load_kv<STREAM>(kp + 64 * kc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vb[j] = load_kv<STREAM>(vp + j * ROW);
   };
-  auto load_unit = [&](uint4 (&kb)[8], uint4 (&vb)[8], int ph0, int ph1, int u) {
-    const char* k0 = tile_ptr(p.kc, ph0, 2 * u) + k_off;
-    const char* k1 = tile_ptr(p.kc, ph1, 2 * u + 1) + k_off;
+  auto consume = [&](const uint4 (&kb)[4], uint4 (&vb)[4], int ch, bool ok) {
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      kb[kc] = load_stream(k0 + 64 * kc);
-      kb[4 + kc] = load_stream(k1 + 64 * kc);
-    }
-    const char* v0 = tile_ptr(p.vc, ph0, 2 * u) + v_off;
-    const char* v1 = tile_ptr(p.vc, ph1, 2 * u + 1) + v_off;
+    for (int kc = 0; kc < 4; ++kc) st = M::mma32(kb[kc], qb[kc], st);
+    const int tok0 = ch * 16 + 4 * kg;   // token of register j is tok0 + j
+    const bool full = ok && (ch * 16 + 16 <= t_end);
+    float sv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vb[j] = load_stream(v0 + j * ROW);
-      vb[4 + j] = load_stream(v1 + j * ROW);
-    }
-  };
-  auto consume = [&](const uint4 (&kb)[8], uint4 (&vb)[8], int u, bool ok0, bool ok1) {
-    f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      st0 = M::mma(kb[kc], qb[kc], st0);
-      st1 = M::mma(kb[4 + kc], qb[kc], st1);
-    }
-    const int tok_base = 32 * u + 4 * kg;  // token of register j is tok_base + 16(j/4) + j%4
-    const bool full = ok0 && ok1 && (32 * u + 32 <= t_end);
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = st0[i] * p.scale_log2;
-      sv[4 + i] = st1[i] * p.scale_log2;
-    }
+    for (int j = 0; j < 4; ++j) sv[j] = st[j] * p.scale_log2;
     if (!full) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool valid = (j < 4 ? ok0 : ok1) && (tok_base + 16 * (j / 4) + (j % 4) < t_end);
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = ok && (tok0 + j < t_end);
         sv[j] = valid ? sv[j] : -INFINITY;
         if (!valid) vb[j] = make_uint4(0, 0, 0, 0);   // masked rows may hold NaN
       }
     }
-    float bm = sv[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) bm = fmaxf(bm, sv[j]);
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(m_run, bm);
@@ -198,66 +183,55 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
       }
     }
     m_run = mn;
-    uint32_t hi[8], lo[8];
+    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const float pj = fast_exp2(sv[j] - ms);
       l_run += pj;
       hi[j] = M::bits(pj);
       lo[j] = M::bits(pj - M::value(hi[j]));
     }
-    const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                 hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-    const uint4 plo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                 lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+    const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint4 bv = tile_column(vb, e);
-      acc[e] = M::mma(phi, bv, acc[e]);
-      acc[e] = M::mma(plo, bv, acc[e]);
+      const uint2 bv = tile_column(vb, e);
+      acc[e] = M::mma16(phi, bv, acc[e]);
+      acc[e] = M::mma16(plo, bv, acc[e]);
     }
   };
 
-  // units of this wave: u_begin + wave + 4*i; table entries of both chunks, one unit per lane
-  for (int base = u_begin + wave; base < u_end; base += 4 * kWave) {
-    const int cnt = min(kWave, (u_end - base + 3) / 4);
-    // A chunk past the context (second half of a ragged last unit) may carry any id here:
-    // ids outside the pool read block 0, and every token of such a chunk is masked.
-    int e0 = e0_first, e1 = e1_first;
-    if (base != u_begin + wave) {
-      e0 = e1 = -1;
-      if (lane < cnt) {
-        const int c0 = 2 * (base + 4 * lane);
-        if (c0 < ch_end) e0 = table[c0 / CPB];
-        if (c0 + 1 < ch_end) e1 = table[(c0 + 1) / CPB];
-      }
+  // chunks of this wave: ch_begin + wave + 4*i; table entries fetched 64 at a time, one per
+  // lane, and broadcast with readlane (the first 64 were fetched above)
+  for (int base = ch_begin + wave; base < ch_end; base += 4 * kWave) {
+    const int cnt = min(kWave, (ch_end - base + 3) / 4);
+    int ent = ent_first;
+    if (base != ch_begin + wave) {
+      const int my_ch = base + 4 * lane;
+      ent = lane < cnt ? table[my_ch / CPB] : -1;
     }
-    auto phys = [&](int ent, int i, bool& ok) {
+    auto phys_of = [&](int i, bool& ok) {
       const int b = __builtin_amdgcn_readlane(ent, i);
-      ok = (unsigned)b < (unsigned)p.num_blocks;  // unused or bad ids read block 0, masked
+      ok = (unsigned)b < (unsigned)p.num_blocks;   // a bad id reads block 0 and is masked
       return ok ? b : 0;
     };
     // Two register buffers, steady-state loads unconditional (see the vector-ALU kernel).
-    uint4 ka[8], va[8], kb2[8], vb2[8];
-    bool a0, a1, b0, b1;
-    auto load_i = [&](uint4 (&kb)[8], uint4 (&vb)[8], int i, bool& o0, bool& o1) {
-      const int x0 = phys(e0, i, o0), x1 = phys(e1, i, o1);
-      load_unit(kb, vb, x0, x1, base + 4 * i);
-    };
-    load_i(ka, va, 0, a0, a1);
+    uint4 ka[4], va[4], kb[4], vb[4];
+    bool oka, okb;
+    load_chunk(ka, va, phys_of(0, oka), base);
     int i = 0;
     for (; i + 2 < cnt; i += 2) {
-      load_i(kb2, vb2, i + 1, b0, b1);
-      consume(ka, va, base + 4 * i, a0, a1);
-      load_i(ka, va, i + 2, a0, a1);
-      consume(kb2, vb2, base + 4 * (i + 1), b0, b1);
+      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      consume(ka, va, base + 4 * i, oka);
+      load_chunk(ka, va, phys_of(i + 2, oka), base + 4 * (i + 2));
+      consume(kb, vb, base + 4 * (i + 1), okb);
     }
     if (i + 1 < cnt) {
-      load_i(kb2, vb2, i + 1, b0, b1);
-      consume(ka, va, base + 4 * i, a0, a1);
-      consume(kb2, vb2, base + 4 * (i + 1), b0, b1);
+      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      consume(ka, va, base + 4 * i, oka);
+      consume(kb, vb, base + 4 * (i + 1), okb);
     } else {
-      consume(ka, va, base + 4 * i, a0, a1);
+      consume(ka, va, base + 4 * i, oka);
     }
   }
 
@@ -309,32 +283,32 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   }
 }
 
-template <DT dt, int BS>
+template <DT dt, int BS, bool ST>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
   switch (gt) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 4>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 8>), dim3(grid), dim3(256), 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<dt, BS, 16, ST>), dim3(grid), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <DT dt>
-hipError_t launch_bs(int bs, int gt, const DecodeParams& p, int grid, hipStream_t st) {
-  if (bs == 16) return launch_gt<dt, 16>(gt, p, grid, st);
-  if (bs == 32) return launch_gt<dt, 32>(gt, p, grid, st);
+hipError_t launch_bs(int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
+  if (bs == 16) return sk ? launch_gt<dt, 16, true>(gt, p, grid, st) : launch_gt<dt, 16, false>(gt, p, grid, st);
+  if (bs == 32) return sk ? launch_gt<dt, 32, true>(gt, p, grid, st) : launch_gt<dt, 32, false>(gt, p, grid, st);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
-                              const DecodeParams& p, int grid, hipStream_t st) {
+                              bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
   if (head_dim != 128) return hipErrorInvalidValue;
   switch (dt) {
-    case DT::F16: return launch_bs<DT::F16>(block_size, heads_per_wg, p, grid, st);
-    case DT::BF16: return launch_bs<DT::BF16>(block_size, heads_per_wg, p, grid, st);
+    case DT::F16: return launch_bs<DT::F16>(block_size, heads_per_wg, stream_kv, p, grid, st);
+    case DT::BF16: return launch_bs<DT::BF16>(block_size, heads_per_wg, stream_kv, p, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,7 +36,7 @@ struct ValuCfg {
   static_assert(BS % 16 == 0, "block size must be a multiple of 16");
 };
 
-template <DT dt, int D, int BS, int GT>
+template <DT dt, int D, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) {
   using C = ValuCfg<dt, D, BS, GT>;
   using E = typename C::E;
@@ -124,9 +124,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     const char* kp = chunk_ptr(p.kc, phys, ch);
     const char* vp = chunk_ptr(p.vc, phys, ch);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kb[i] = load_stream(kp + i * TPI * C::ROW_BYTES);
+    for (int i = 0; i < NI; ++i) kb[i] = load_kv<STREAM>(kp + i * TPI * C::ROW_BYTES);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vb[i] = load_stream(vp + i * TPI * C::ROW_BYTES);
+    for (int i = 0; i < NI; ++i) vb[i] = load_kv<STREAM>(vp + i * TPI * C::ROW_BYTES);
   };
   auto consume = [&](const uint4 (&kb)[NI], const uint4 (&vb)[NI], int ch, bool ok) {
     const int tok0 = ch * 16 + row;
@@ -285,35 +285,41 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
 }
 
-template <DT dt, int D, int BS>
+template <DT dt, int D, int BS, bool ST>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
   switch (gt) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 1>), dim3(grid), dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 2>), dim3(grid), dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 4>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 8>), dim3(grid), dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 1, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 2, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <DT dt, int D, int BS>
+hipError_t launch_st(bool stream_kv, int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  return stream_kv ? launch_gt<dt, D, BS, true>(gt, p, grid, st)
+                   : launch_gt<dt, D, BS, false>(gt, p, grid, st);
+}
+
 template <DT dt>
-hipError_t launch_dt(int d, int bs, int gt, const DecodeParams& p, int grid, hipStream_t st) {
-  if (d == 64 && bs == 16) return launch_gt<dt, 64, 16>(gt, p, grid, st);
-  if (d == 64 && bs == 32) return launch_gt<dt, 64, 32>(gt, p, grid, st);
-  if (d == 128 && bs == 16) return launch_gt<dt, 128, 16>(gt, p, grid, st);
-  if (d == 128 && bs == 32) return launch_gt<dt, 128, 32>(gt, p, grid, st);
+hipError_t launch_dt(int d, int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
+  if (d == 64 && bs == 16) return launch_st<dt, 64, 16>(sk, gt, p, grid, st);
+  if (d == 64 && bs == 32) return launch_st<dt, 64, 32>(sk, gt, p, grid, st);
+  if (d == 128 && bs == 16) return launch_st<dt, 128, 16>(sk, gt, p, grid, st);
+  if (d == 128 && bs == 32) return launch_st<dt, 128, 32>(sk, gt, p, grid, st);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
-                              const DecodeParams& p, int grid, hipStream_t st) {
+                              bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
   switch (dt) {
-    case DT::F32: return launch_dt<DT::F32>(head_dim, block_size, heads_per_wg, p, grid, st);
-    case DT::F16: return launch_dt<DT::F16>(head_dim, block_size, heads_per_wg, p, grid, st);
-    case DT::BF16: return launch_dt<DT::BF16>(head_dim, block_size, heads_per_wg, p, grid, st);
+    case DT::F32: return launch_dt<DT::F32>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
+    case DT::F16: return launch_dt<DT::F16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
+    case DT::BF16: return launch_dt<DT::BF16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -17,6 +17,7 @@ HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "pa.h"
 
 PA_OK = 0
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+PA_DECODE_SHARED_BLOCKS = 0x1
 
 
 class PaError(RuntimeError):
@@ -36,9 +37,10 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (_c_size, [_c_int] * 7),
     "pa_decode": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _p, _c_size, _p]),
     "pa_decode_ex": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _p, _c_size,
-                                                          _c_int, _p]),
+                                                          _c_int, ctypes.c_uint32, _p]),
     "pa_decode_partitions": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _p,
-                                                                  _c_size, _c_int, _p]),
+                                                                  _c_size, _c_int, ctypes.c_uint32,
+                                                                  _p]),
     "pa_decode_merge": (_c_int, [_p, _p] + [_c_int] * 8 + [_p, _c_size, _p]),
     "pa_reshape_and_cache": (_c_int, [_p] * 5 + [_c_int] * 6 + [_p]),
     "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
@@ -143,8 +145,9 @@ def _decode_shapes(out, query, key_cache, value_cache, block_tables, context_len
 
 
 def decode(out, query, key_cache, value_cache, block_tables, context_lens, scale, *,
-           partition_size=0, kernel="auto", workspace=None, stream=None):
-    """pa_decode_ex: paged decode attention into ``out`` ([S, Hq, d])."""
+           partition_size=0, kernel="auto", shared_blocks=False, workspace=None, stream=None):
+    """pa_decode_ex: paged decode attention into ``out`` ([S, Hq, d]).  ``shared_blocks``
+    sets PA_DECODE_SHARED_BLOCKS (blocks read by several sequences: cache-allocating loads)."""
     import torch
     dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
     S, Hq, Hkv, D, BS, NB, maxb = _decode_shapes(out, query, key_cache, value_cache, block_tables,
@@ -156,13 +159,15 @@ def decode(out, query, key_cache, value_cache, block_tables, context_lens, scale
     _check(load().pa_decode_ex(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS, NB, maxb,
                                float(scale), _dtype_code(query), int(partition_size),
-                               _ptr(workspace), wsb, KERNELS[kernel], _stream(dev, stream)),
+                               _ptr(workspace), wsb, KERNELS[kernel],
+                               PA_DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(dev, stream)),
            "pa_decode_ex")
     return out
 
 
 def decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                      workspace, *, partition_size=0, kernel="auto", stream=None):
+                      workspace, *, partition_size=0, kernel="auto", shared_blocks=False,
+                      stream=None):
     """pa_decode_partitions: the first of pa_decode's two launches."""
     dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
     S, Hq, Hkv, D, BS, NB, maxb = _decode_shapes(out, query, key_cache, value_cache, block_tables,
@@ -172,6 +177,7 @@ def decode_partitions(out, query, key_cache, value_cache, block_tables, context_
                                        _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS,
                                        NB, maxb, float(scale), _dtype_code(query),
                                        int(partition_size), _ptr(workspace), wsb, KERNELS[kernel],
+                                       PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                        _stream(dev, stream)), "pa_decode_partitions")
 
 

@@ -53,10 +53,12 @@ class Uploaded:
         self.pairs = torch.from_numpy(np.ascontiguousarray(case.block_mapping, np.int64).reshape(-1, 2)).to(dev)
         self.out = torch.empty_like(self.q)
 
-    def decode(self, kernel="auto", partition_size=0):
+    def decode(self, kernel="auto", partition_size=0, shared_blocks=None):
         import torch
+        if shared_blocks is None:
+            shared_blocks = bool(self.case.spec.shared_prefix)
         ops.decode(self.out, self.q, self.kc, self.vc, self.bt, self.cl, float(self.case.scale),
-                   partition_size=partition_size, kernel=kernel)
+                   partition_size=partition_size, kernel=kernel, shared_blocks=shared_blocks)
         torch.cuda.synchronize()
         return W.from_torch(self.out, self.case.dtype)
 

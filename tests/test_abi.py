@@ -39,12 +39,13 @@ def test_status_strings_and_version(lib):
 
 def _decode(lib, **kw):
     a = dict(out=1, q=1, kc=1, vc=1, bt=1, cl=1, S=4, Hq=8, Hkv=2, D=128, BS=16, NB=100, maxb=8,
-             scale=0.1, dtype=2, P=0, ws=None, wsb=0, kernel=0)
+             scale=0.1, dtype=2, P=0, ws=None, wsb=0, kernel=0, flags=0)
     a.update(kw)
     p = lambda v: ctypes.c_void_p(v) if v else None
     return lib.pa_decode_ex(p(a["out"]), p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), p(a["cl"]),
                             a["S"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"], a["maxb"],
-                            a["scale"], a["dtype"], a["P"], p(a["ws"]), a["wsb"], a["kernel"], None)
+                            a["scale"], a["dtype"], a["P"], p(a["ws"]), a["wsb"], a["kernel"],
+                            a["flags"], None)
 
 
 def test_decode_argument_errors(lib):
@@ -63,6 +64,8 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, kernel=2, dtype=0) == 3      # matrix-core path needs f16/bf16
     assert _decode(lib, kernel=2, Hq=6, Hkv=3) == 3  # group of 2
     assert _decode(lib, kernel=2, D=64) == 3
+    assert _decode(lib, flags=0x2) == 3              # unknown flag bit
+    assert _decode(lib, flags=0x1, out=0) == 1       # the shared-blocks flag itself is accepted
     assert _decode(lib, maxb=64, P=64) == 4          # split needs a workspace
     assert _decode(lib, maxb=64, P=64, ws=1, wsb=16) == 4
     assert _decode(lib, S=0, out=0, q=0) == 0        # empty batch: no-op

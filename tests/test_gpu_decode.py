@@ -27,7 +27,7 @@ def _case(dtype, D, BS, Hq, Hkv, lengths=EDGE_LENGTHS, seed=100, **kw):
 
 
 def _mfma_ok(dtype, D, Hq, Hkv, P):
-    return dtype in ("f16", "bf16") and D == 128 and (Hq // Hkv) % 4 == 0 and P % 32 == 0
+    return dtype in ("f16", "bf16") and D == 128 and (Hq // Hkv) % 4 == 0 and P % 16 == 0
 
 
 @pytest.mark.parametrize("partition", [0, 64, 48])
@@ -148,3 +148,16 @@ def test_split_and_single_pass_agree():
     vmax = live_vmax(c)
     for P in (32, 64, 512, 4096):
         assert_attention_close(u.decode("valu", P), ref, "bf16", vmax, f"P={P}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_shared_blocks_flag_changes_nothing(kernel):
+    """PA_DECODE_SHARED_BLOCKS only changes the load cache policy: identical bits."""
+    dev = need_gpu()
+    c = _case("bf16", 128, 16, 8, 2, lengths=[7, 300, 1000, 64], seed=17)
+    u = Uploaded(c, dev)
+    for P in (0, 64):
+        a = u.decode(kernel, P, shared_blocks=False)
+        b = u.decode(kernel, P, shared_blocks=True)
+        assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
+        assert_attention_close(b, oracle_decode(c), "bf16", live_vmax(c), f"shared-flag/{kernel}/P{P}")
