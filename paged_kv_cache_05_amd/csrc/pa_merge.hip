@@ -52,12 +52,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
       w = v.y * fast_exp2(v.x - ms);
     }
     const int cnt = min(kWave, np - i0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      L += wj;
-      const float* src = po + (size_t)(i0 + j) * D;
+    // eight partitions per step: their loads are issued together, then accumulated in
+    // partition order (the order, and so the result, does not depend on the unrolling)
+    constexpr int U = 8;
+    for (int j0 = 0; j0 < cnt; j0 += U) {
+      float v[U][DPL];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + u, cnt - 1);   // in-bounds; surplus slots get weight 0 below
+        const float* src = po + (size_t)(i0 + j) * D;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) v[u][e] = src[e];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (j0 + u < cnt) {
+          const float wj = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + u));
+          L += wj;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wj, v[u][e], acc[e]);
+        }
+      }
     }
   }
   const float inv = 1.0f / L;
