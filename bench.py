@@ -220,6 +220,33 @@ def calibrate_copy(dev, steps):
                       "GBps_read_plus_write": round(2 * moved / ms / 1e6, 1)}), flush=True)
 
 
+def measure_swap(dev, steps):
+    """swap_blocks over the host link: 2048 Llama-7B-shaped blocks (32 heads x 16 x 128 bf16,
+    K and V: 256 KiB per block) GPU -> pinned host and back."""
+    import torch
+    nb, shape = 2048, (2048, 32, 16, 128)
+    gk = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    gv = torch.zeros_like(gk)
+    hk = torch.zeros(shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros(shape, dtype=torch.bfloat16).pin_memory()
+    ident = torch.arange(nb, dtype=torch.int64)
+    pairs = torch.stack([ident.flip(0), ident], 1).to(dev)
+    moved = nb * 2 * 32 * 16 * 128 * 2
+    res = {}
+    for name, args in (("gpu_to_host", (gk, gv, hk, hv)), ("host_to_gpu", (hk, hv, gk, gv))):
+        ops.swap_blocks(*args, pairs)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            ops.swap_blocks(*args, pairs)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        res[name] = {"ms": round(ms, 4), "GBps": round(moved / ms / 1e6, 2), "bytes": moved}
+    return res
+
+
 def run_workload(name, dev, steps, warmup, kernel):
     import torch
     case = W.build_case(W.CONFIGS[name], device=dev)
@@ -320,6 +347,9 @@ def main(argv=None):
                          "kernel": chosen_kernel(c2, args.kernel)}
         del c2
     if detail:
+        del step
+        torch.cuda.empty_cache()
+        detail["swap_blocks"] = measure_swap(dev, max(3, args.steps // 4))
         rec["detail"] = detail
     if snaps is not None:
         rec["cpu_baseline"] = cpu_baseline(case, snaps, args.cpu_seconds)

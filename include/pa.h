@@ -209,6 +209,32 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bloc
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
 
+/*
+ * pa_swap_blocks — whole-block copies between two different pools: the GPU pool and a pool in
+ * pinned host memory, in either direction.
+ *
+ * The block engine keeps block pools on both the GPU and the CPU; a preempted sequence's blocks
+ * can be swapped out to the CPU pool and back in when it resumes (xasun.com summary §二,
+ * block-engine and scheduler items).  For each pair p, with (src, dst) = (block_mapping[2p],
+ * block_mapping[2p+1]), block src of the source pools (every KV head, every slot) is copied to
+ * block dst of the destination pools.  Pairs with src outside [0, src_num_blocks) or dst outside
+ * [0, dst_num_blocks) are skipped.  Bits are copied unchanged; destinations must be distinct.
+ *
+ *   src_key_cache, src_value_cache  [src_num_blocks][num_kv_heads][block_size][head_dim]
+ *   dst_key_cache, dst_value_cache  [dst_num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_mapping  int64 [num_pairs][2]
+ * Every pointer must be usable by the GPU: device memory, or host memory allocated pinned
+ * (hipHostMalloc, or a torch tensor created with pin_memory=True), which the kernel reads or
+ * writes over the host link.  The pools are not synchronised with the host: the caller waits
+ * on `stream` before reading a host pool.
+ * Supported: num_kv_heads * block_size * head_dim * sizeof(dtype) a multiple of 16 bytes.
+ */
+pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                         int32_t src_num_blocks, void* dst_key_cache, void* dst_value_cache,
+                         int32_t dst_num_blocks, const int64_t* block_mapping, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

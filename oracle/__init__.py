@@ -15,4 +15,5 @@ from .pa_oracle import (  # noqa: F401
     resolve_sequence,
     slot_utilization,
     storage_to_f64,
+    swap_blocks_ref,
 )

@@ -246,6 +246,24 @@ def reshape_and_cache_ref(key, value, key_cache, value_cache, slot_mapping, bloc
     return kc, vc
 
 
+def swap_blocks_ref(src_key, src_value, dst_key, dst_value, block_mapping):
+    """Copies of the destination pools where block dst receives the whole of source block src
+    (every head, every slot) for each (src, dst) pair.  Source and destination are different
+    pools (the GPU pool and the host pool used to swap preempted sequences out and back in:
+    xasun.com summary §二, block-engine and scheduler items).  Pairs with an id outside its
+    pool are skipped; bits are copied unchanged."""
+    kd = np.array(dst_key, copy=True)
+    vd = np.array(dst_value, copy=True)
+    ns, nd = src_key.shape[0], kd.shape[0]
+    for src, dst in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        src, dst = int(src), int(dst)
+        if not (0 <= src < ns and 0 <= dst < nd):
+            continue
+        kd[dst] = src_key[src]
+        vd[dst] = src_value[src]
+    return kd, vd
+
+
 def copy_blocks_ref(key_cache, value_cache, block_mapping):
     """Copies of the pools where block dst receives the whole of block src (every head,
     every slot) for each (src, dst) pair, all read from the pools as they were before the

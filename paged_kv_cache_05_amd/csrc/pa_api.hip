@@ -285,9 +285,32 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bloc
   if (num_pairs == 0) return PA_OK;
   if (!key_cache || !value_cache || !block_mapping) return PA_ERR_NULL_PTR;
   (void)hipGetLastError();
-  return launch_status(pa::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
-                                              block_bytes / 16, num_blocks,
-                                              reinterpret_cast<hipStream_t>(stream)));
+  return launch_status(pa::launch_block_copy(key_cache, value_cache, key_cache, value_cache,
+                                             block_mapping, num_pairs, block_bytes / 16,
+                                             num_blocks, num_blocks,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
+                         int32_t src_num_blocks, void* dst_key_cache, void* dst_value_cache,
+                         int32_t dst_num_blocks, const int64_t* block_mapping, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         pa_dtype dtype, void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      src_num_blocks < 0 || dst_num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  const long block_bytes = (long)num_kv_heads * block_size * head_dim * elem_bytes(dt);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_mapping)
+    return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_block_copy(src_key_cache, src_value_cache, dst_key_cache,
+                                             dst_value_cache, block_mapping, num_pairs,
+                                             block_bytes / 16, src_num_blocks, dst_num_blocks,
+                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
-// KV-cache writers: reshape_and_cache (store each new token at its slot) and copy_blocks
-// (copy-on-write of whole blocks).  Both are pure data movement in 16-byte vectors; bits are
+// KV-cache writers: reshape_and_cache (store each new token at its slot), copy_blocks
+// (copy-on-write of whole blocks) and swap_blocks (whole blocks between the GPU pool and a
+// pinned host pool).  All are pure data movement in 16-byte vectors; bits are
 // copied unchanged.
 //
 // reshape_and_cache: each decode step appends the new token's K/V to the cache
@@ -7,6 +8,8 @@
 // workflow).  Token i goes to block slot/bs, offset slot%bs, every KV head.
 // copy_blocks: shared blocks are reference-counted and copied before a write (UltraLAB
 // summary of Kwon et al. (xasun.com) §一 and §二, sharing item).
+// swap_blocks: a preempted sequence's blocks move to a CPU block pool and back (same page,
+// §二: block pools on both GPU and CPU; recovery by swapping).
 #include "pa_common.h"
 
 namespace pa {
@@ -36,20 +39,23 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 constexpr int kCopyUnroll = 4;
 constexpr int kCopyVecsPerWg = 256 * kCopyUnroll;
 
-// grid.x = pairs * 2 (K, V) * chunks; each workgroup copies up to 16 KiB of one block.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc,
-                                                          uint4* __restrict__ vc,
-                                                          const int64_t* __restrict__ mapping,
-                                                          int64_t block_vecs, int chunks,
-                                                          int num_blocks) {
+// Whole-block copies between two pools (the same pool for copy-on-write, the GPU pool and a
+// pinned host pool for swapping).  grid.x = pairs * 2 (K, V) * chunks; each workgroup copies up
+// to 16 KiB of one block with four independent 16-byte loads per lane.
+__global__ __launch_bounds__(256) void block_copy_kernel(const uint4* __restrict__ src_k,
+                                                         const uint4* __restrict__ src_v,
+                                                         uint4* __restrict__ dst_k,
+                                                         uint4* __restrict__ dst_v,
+                                                         const int64_t* __restrict__ mapping,
+                                                         int64_t block_vecs, int chunks,
+                                                         int src_blocks, int dst_blocks) {
   const int chunk = blockIdx.x % chunks;
   const int which = (blockIdx.x / chunks) & 1;
   const int pair = blockIdx.x / (2 * chunks);
   const int64_t src = mapping[2 * pair], dst = mapping[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  uint4* pool = which ? vc : kc;
-  const uint4* s = pool + src * block_vecs;
-  uint4* d = pool + dst * block_vecs;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s = (which ? src_v : src_k) + src * block_vecs;
+  uint4* d = (which ? dst_v : dst_k) + dst * block_vecs;
   const int64_t v0 = (int64_t)chunk * kCopyVecsPerWg + threadIdx.x;
   uint4 r[kCopyUnroll];
 #pragma unroll
@@ -77,14 +83,16 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* kc, void* vc, const int64_t* mapping, int num_pairs,
-                              int64_t block_vecs, int num_blocks, hipStream_t st) {
+hipError_t launch_block_copy(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int64_t* mapping, int num_pairs, int64_t block_vecs,
+                             int src_blocks, int dst_blocks, hipStream_t st) {
   if (num_pairs <= 0) return hipSuccess;
   const int chunks = (int)((block_vecs + kCopyVecsPerWg - 1) / kCopyVecsPerWg);
   const int64_t grid = (int64_t)num_pairs * 2 * chunks;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, st, (uint4*)kc,
-                     (uint4*)vc, mapping, block_vecs, chunks, num_blocks);
+  hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)grid), dim3(256), 0, st,
+                     (const uint4*)src_k, (const uint4*)src_v, (uint4*)dst_k, (uint4*)dst_v,
+                     mapping, block_vecs, chunks, src_blocks, dst_blocks);
   return hipGetLastError();
 }
 

@@ -186,7 +186,8 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
                                     const int64_t* slots, int num_tokens, int row_vecs,
                                     int block_size, int num_blocks, int num_kv_heads,
                                     hipStream_t st);
-hipError_t launch_copy_blocks(void* kc, void* vc, const int64_t* mapping, int num_pairs,
-                              int64_t block_vecs, int num_blocks, hipStream_t st);
+hipError_t launch_block_copy(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int64_t* mapping, int num_pairs, int64_t block_vecs,
+                             int src_blocks, int dst_blocks, hipStream_t st);
 
 }  // namespace pa

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "pa_decode_merge": (_c_int, [_p, _p] + [_c_int] * 8 + [_p, _c_size, _p]),
     "pa_reshape_and_cache": (_c_int, [_p] * 5 + [_c_int] * 6 + [_p]),
     "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
+    "pa_swap_blocks": (_c_int, [_p, _p, _c_int, _p, _p, _c_int, _p] + [_c_int] * 5 + [_p]),
 }
 
 
@@ -223,3 +224,33 @@ def copy_blocks(key_cache, value_cache, block_mapping, *, stream=None):
     _check(load().pa_copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(block_mapping),
                                  block_mapping.shape[0], Hkv, D, BS, NB, _dtype_code(key_cache),
                                  _stream(dev, stream)), "pa_copy_blocks")
+
+
+def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, *, stream=None):
+    """pa_swap_blocks: copy whole blocks between two pools (GPU <-> pinned host), per row
+    (src, dst) of block_mapping [P, 2] (int64, on the GPU or pinned).  Host pools must be
+    pinned; the copy is asynchronous on the GPU stream."""
+    import torch
+    gpu = [t for t in (src_key, src_value, dst_key, dst_value, block_mapping) if t.is_cuda]
+    if not gpu:
+        raise ValueError("at least one pool must be on the GPU")
+    dev = gpu[0].device
+    for t in (src_key, src_value, dst_key, dst_value, block_mapping):
+        if not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous")
+        if t.is_cuda and t.device != dev:
+            raise ValueError("GPU tensors are on different devices")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError("host tensors must be pinned (pin_memory=True)")
+    NS, Hkv, BS, D = src_key.shape
+    ND = dst_key.shape[0]
+    if tuple(src_value.shape) != tuple(src_key.shape) or tuple(dst_value.shape) != tuple(dst_key.shape) \
+            or tuple(dst_key.shape[1:]) != (Hkv, BS, D):
+        raise ValueError("pools must be [blocks, num_kv_heads, block_size, head_dim] with equal block shape")
+    if not (src_key.dtype == src_value.dtype == dst_key.dtype == dst_value.dtype):
+        raise TypeError("all pools must share one element type")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [num_pairs, 2]")
+    _check(load().pa_swap_blocks(_ptr(src_key), _ptr(src_value), NS, _ptr(dst_key), _ptr(dst_value),
+                                 ND, _ptr(block_mapping), block_mapping.shape[0], Hkv, D, BS,
+                                 _dtype_code(src_key), _stream(dev, stream)), "pa_swap_blocks")

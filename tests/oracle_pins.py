@@ -373,4 +373,42 @@ def pin_copy_on_write(O):
         assert np.max(np.abs(out[s] - ref)) <= 1e-12, s
 
 
+
+
+def pin_swap_blocks(O):
+    """Swapping blocks to a second pool copies them bit for bit (against a per-element loop);
+    swapping a sequence out and back into different blocks, with its table rewritten, leaves
+    its decode output unchanged (recovery by swapping is lossless)."""
+    rng = np.random.default_rng(8)
+    NB, NH, H, bs, d = 10, 6, 2, 16, 8
+    gk = rng.standard_normal((NB, H, bs, d)).astype(np.float16)
+    gv = rng.standard_normal((NB, H, bs, d)).astype(np.float16)
+    hk = np.zeros((NH, H, bs, d), np.float16)
+    hv = np.zeros((NH, H, bs, d), np.float16)
+    pairs = np.array([[4, 0], [7, 3], [1, 5], [-1, 2], [3, NH]], np.int64)
+    k2, v2 = O.swap_blocks_ref(gk, gv, hk, hv, pairs)
+    kl, vl = hk.copy(), hv.copy()
+    for s, t in pairs:
+        if 0 <= s < NB and 0 <= t < NH:
+            for a in range(H):
+                for b in range(bs):
+                    for j in range(d):
+                        kl[t, a, b, j] = gk[s, a, b, j]
+                        vl[t, a, b, j] = gv[s, a, b, j]
+    assert np.array_equal(k2.view(np.uint16), kl.view(np.uint16))
+    assert np.array_equal(v2.view(np.uint16), vl.view(np.uint16))
+    assert np.array_equal(hk, np.zeros_like(hk)), "the input pool must not be modified"
+    # a sequence in blocks [4, 7, 1] swapped out to host blocks [0, 3, 5], then back in to GPU
+    # blocks [9, 2, 6] of a pool where those held other data
+    q = rng.standard_normal((1, H, d)).astype(np.float16)
+    n = 40
+    before = O.decode_ref(q, gk, gv, np.array([[4, 7, 1]], np.int32), np.array([n], np.int32),
+                          bs, np.float32(0.35), "f16")
+    back = np.array([[0, 9], [3, 2], [5, 6]], np.int64)
+    gk2, gv2 = O.swap_blocks_ref(k2, v2, gk, gv, back)
+    after = O.decode_ref(q, gk2, gv2, np.array([[9, 2, 6]], np.int32), np.array([n], np.int32),
+                         bs, np.float32(0.35), "f16")
+    assert np.array_equal(before, after)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

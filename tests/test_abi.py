@@ -106,3 +106,11 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         ops.decode(x, x, kc, kc, torch.zeros(2, 1, dtype=torch.int32),
                    torch.ones(2, dtype=torch.int32), 0.125)
+
+
+def test_swap_blocks_argument_errors(lib):
+    p = ctypes.c_void_p(1)
+    assert lib.pa_swap_blocks(p, p, 4, p, None, 4, p, 2, 2, 64, 16, 0, None) == 1
+    assert lib.pa_swap_blocks(p, p, -1, p, p, 4, p, 2, 2, 64, 16, 0, None) == 2
+    assert lib.pa_swap_blocks(p, p, 4, p, p, 4, p, 2, 1, 3, 1, 1, None) == 3     # 6-byte blocks
+    assert lib.pa_swap_blocks(None, None, 4, None, None, 4, None, 0, 2, 64, 16, 0, None) == 0

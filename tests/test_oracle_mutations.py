@@ -48,6 +48,8 @@ MUTATIONS = [
      "return int(num_tokens) // int(block_size)"),
     ("utilisation denominator", "reserved = sum(num_blocks_for(n, block_size) * block_size for n in lengths)",
      "reserved = sum(lengths)"),
+    ("swap writes the source", "        kd[dst] = src_key[src]\n", "        kd[src % nd] = src_key[dst % ns]\n"),
+    ("swap bounds use one pool", "if not (0 <= src < ns and 0 <= dst < nd):", "if not (0 <= src < nd and 0 <= dst < nd):"),
 ]
 
 
