@@ -10,6 +10,7 @@ from .pa_oracle import (  # noqa: F401
     decode_split_ref,
     f64_to_storage,
     kv_bytes_per_token,
+    prefill_ref,
     num_blocks_for,
     reshape_and_cache_ref,
     resolve_sequence,

@@ -1,4 +1,5 @@
-"""Plain float64 CPU oracle for paged decode attention, reshape_and_cache and copy_blocks.
+"""Plain float64 CPU oracle for paged decode attention, prefill attention over the paged
+cache, reshape_and_cache, copy_blocks and swap_blocks.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` may import, call or run anything here.  The GPU library never calls it,
@@ -42,7 +43,9 @@ float64 SDPA on tiny inputs; paged == contiguous; invariance under any permutati
 physical placement; all-equal keys and scale 0 give mean(V); one-token context gives V
 exactly; poisoned unused slots/blocks/table entries change nothing; split+merge == unsplit;
 the pages' per-token KV and page-count arithmetic (``tests/golden/``); reshape/copy against a
-flat-slot formulation and a per-element loop; copy-on-write round trips.  A mutation test
+flat-slot formulation and a per-element loop; copy-on-write round trips; for prefill, decimal
+brute force over the causal prefix, torch's float64 causal SDPA on whole prompts, every row
+equal to a decode at its position, and invariance under re-chunking.  A mutation test
 plants mistakes in a copy of this file and checks that some pin fails for each.
 """
 
@@ -280,3 +283,45 @@ def copy_blocks_ref(key_cache, value_cache, block_mapping):
         kc[dst] = k0[src]
         vc[dst] = v0[src]
     return kc, vc
+
+
+# ---------------------------------------------------------------------------------------
+# prefill attention over the paged cache
+# ---------------------------------------------------------------------------------------
+def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+                block_size, scale, dtype: str) -> np.ndarray:
+    """Causal attention of a chunk of new tokens per sequence over the paged cache, float64
+    ``[T, Hq, d]``.
+
+    Prefill is the compute-heavy phase that precedes decoding (xasun.com summary §三, table row
+    on the compute pattern), and it may be cut into chunks (the chunked-prefill switch in the
+    jsqmd.com page's vLLM usage example).  Sequence s owns query rows
+    ``query_start_loc[s] .. query_start_loc[s+1]-1`` (L rows).  Its ``context_lens[s]`` = n
+    cached tokens already include those rows' own K/V (reshape_and_cache runs first), so the
+    chunk's token i sits at position n - L + i and, as a decoded token at that position would,
+    attends to the positions 0 .. n - L + i.  A sequence with n < L has no valid placement:
+    its rows are zero.  Rows no sequence owns are zero.
+    """
+    T, Hq, d = query.shape
+    Hkv = key_cache.shape[1]
+    if Hq % Hkv:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    out = np.zeros((T, Hq, d), dtype=np.float64)
+    for s in range(len(qsl) - 1):
+        q0, q1 = int(qsl[s]), int(qsl[s + 1])
+        L, n = q1 - q0, int(context_lens[s])
+        if L <= 0 or n < L:
+            continue
+        K = resolve_sequence(key_cache, block_tables[s], n, block_size, dtype)
+        V = resolve_sequence(value_cache, block_tables[s], n, block_size, dtype)
+        q = storage_to_f64(query[q0:q1], dtype)
+        for i in range(L):
+            last = n - L + i               # the token's own position
+            for h in range(Hq):
+                kv = h // G
+                out[q0 + i, h] = _softmax_weighted_sum(K[kv, :last + 1], V[kv, :last + 1],
+                                                       q[i, h], sc)
+    return out

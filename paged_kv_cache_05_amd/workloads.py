@@ -117,21 +117,27 @@ CONFIGS = {
 }
 
 
-def draw_lengths(spec: CaseSpec, rng: np.random.Generator) -> np.ndarray:
-    kind = spec.lengths[0]
+def draw_from(lengths: tuple, count: int, rng: np.random.Generator) -> np.ndarray:
+    """``count`` integers from a length spec: ("uniform", lo, hi) inclusive,
+    ("lognormal", median, sigma, lo, hi) rounded and clipped, ("fixed", [n0, n1, ...])."""
+    kind = lengths[0]
     if kind == "uniform":
-        lo, hi = spec.lengths[1], spec.lengths[2]
-        return rng.integers(lo, hi + 1, size=spec.num_seqs).astype(np.int64)
+        lo, hi = lengths[1], lengths[2]
+        return rng.integers(lo, hi + 1, size=count).astype(np.int64)
     if kind == "lognormal":
-        median, sigma, lo, hi = spec.lengths[1:]
-        x = rng.lognormal(mean=math.log(median), sigma=sigma, size=spec.num_seqs)
+        median, sigma, lo, hi = lengths[1:]
+        x = rng.lognormal(mean=math.log(median), sigma=sigma, size=count)
         return np.clip(np.rint(x), lo, hi).astype(np.int64)
     if kind == "fixed":
-        v = np.asarray(spec.lengths[1], dtype=np.int64)
-        if v.shape != (spec.num_seqs,):
+        v = np.asarray(lengths[1], dtype=np.int64)
+        if v.shape != (count,):
             raise ValueError("fixed lengths must have one entry per sequence")
         return v.copy()
-    raise ValueError(f"unknown length spec {spec.lengths!r}")
+    raise ValueError(f"unknown length spec {lengths!r}")
+
+
+def draw_lengths(spec: CaseSpec, rng: np.random.Generator) -> np.ndarray:
+    return draw_from(spec.lengths, spec.num_seqs, rng)
 
 
 # ---------------------------------------------------------------------------------------
@@ -379,3 +385,85 @@ def _device_pool(shape, dtype, seed_seq, device):
         out[b0:b1] = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device,
                                  dtype=torch.float32).to(out.dtype)
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# prefill (a chunk of new tokens per sequence, attending causally over the paged cache)
+# ---------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PrefillSpec:
+    name: str
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    block_size: int
+    prefix_lengths: tuple              # tokens cached before this chunk (length-spec forms)
+    chunk_lengths: tuple               # new tokens in this chunk
+    pool_fill: float = 0.9
+    max_blocks_per_seq: int | None = None
+
+
+PREFILL_CONFIGS = {
+    # Llama-7B-shaped chunked prefill: 512-token chunks on top of 0..1536 cached tokens
+    "prefill_llama7b": PrefillSpec("prefill_llama7b", 6, 32, 32, 32, 128, "bf16", 16,
+                                   ("uniform", 0, 1536), ("fixed", [512] * 32)),
+    # grouped-query heads, ragged chunks, long prefixes
+    "prefill_gqa": PrefillSpec("prefill_gqa", 7, 8, 32, 8, 128, "bf16", 16,
+                               ("uniform", 0, 3000), ("uniform", 1, 700)),
+}
+
+
+@dataclass
+class PrefillCase:
+    spec: PrefillSpec
+    pool: DecodeCase                   # pools, tables, context lengths (its query is unused)
+    query: np.ndarray                  # [T, Hq, d] storage, the chunks packed back to back
+    query_start_loc: np.ndarray        # int32 [S + 1]
+    query_lens: np.ndarray             # int64 [S]
+    context_lens: np.ndarray           # int32 [S]: prefix + chunk (the chunk is already cached)
+    max_query_len: int
+
+    @property
+    def dtype(self):
+        return self.spec.dtype
+
+    @property
+    def block_size(self):
+        return self.spec.block_size
+
+    @property
+    def scale(self):
+        return self.pool.scale
+
+
+def build_prefill_case(spec: PrefillSpec, *, device=None, poison=False, table_fill=-1,
+                       keep_contiguous=False) -> PrefillCase:
+    """Generate one chunked-prefill call: every sequence's prefix and chunk are in the pool
+    (the chunk written by reshape_and_cache beforehand), and the chunk's queries are packed
+    into ``query`` in sequence order."""
+    ss = np.random.SeedSequence(spec.seed)
+    c_pre, c_chunk, c_q, c_pool = ss.spawn(4)
+    S = spec.num_seqs
+    pre = draw_from(spec.prefix_lengths, S, np.random.default_rng(c_pre))
+    chunk = draw_from(spec.chunk_lengths, S, np.random.default_rng(c_chunk))
+    if np.any(pre < 0) or np.any(chunk < 0):
+        raise ValueError("lengths must be non-negative")
+    ctx = pre + chunk
+    pool_spec = CaseSpec(spec.name, int(c_pool.generate_state(1)[0]), S, spec.num_heads,
+                         spec.num_kv_heads, spec.head_dim, spec.dtype, spec.block_size,
+                         ("fixed", [int(n) for n in ctx]), pool_fill=spec.pool_fill,
+                         new_tokens=("free", 0), max_blocks_per_seq=spec.max_blocks_per_seq)
+    pool = build_case(pool_spec, device=device, poison=poison, table_fill=table_fill,
+                      keep_contiguous=keep_contiguous)
+    qsl = np.zeros(S + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(chunk)
+    T = int(qsl[-1])
+    q32 = np.random.default_rng(c_q).standard_normal((T, spec.num_heads, spec.head_dim),
+                                                     dtype=np.float32)
+    return PrefillCase(spec=spec, pool=pool, query=round_to_storage(q32, spec.dtype),
+                       query_start_loc=qsl, query_lens=chunk.astype(np.int64),
+                       context_lens=ctx.astype(np.int32),
+                       max_query_len=int(chunk.max()) if S else 0)

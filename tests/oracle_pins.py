@@ -411,4 +411,123 @@ def pin_swap_blocks(O):
     assert np.array_equal(before, after)
 
 
+# ---------------------------------------------------------------------------------------
+# prefill attention over the paged cache
+# ---------------------------------------------------------------------------------------
+def _pcase(S=3, Hq=4, Hkv=2, d=8, dtype="f32", bs=16, prefix=(0, 5, 20), chunk=(4, 1, 13),
+           seed=41, **kw):
+    spec = W.PrefillSpec("pin", seed, S, Hq, Hkv, d, dtype, bs, ("fixed", list(prefix)),
+                         ("fixed", list(chunk)), **kw)
+    return W.build_prefill_case(spec, keep_contiguous=True)
+
+
+def _prun(O, c, **over):
+    args = dict(query=c.query, key_cache=c.pool.key_cache, value_cache=c.pool.value_cache,
+                block_tables=c.pool.block_tables, query_start_loc=c.query_start_loc,
+                context_lens=c.context_lens, block_size=c.block_size, scale=c.scale,
+                dtype=c.dtype)
+    args.update(over)
+    return O.prefill_ref(**args)
+
+
+def pin_prefill_brute_force(O):
+    """Decimal brute force: the chunk's token i of a sequence with prefix p attends to the
+    contiguous tokens 0 .. p + i, over GQA heads, bf16 and peaky scores."""
+    for dtype, seed in (("f32", 41), ("bf16", 42)):
+        c = _pcase(dtype=dtype, seed=seed)
+        out = _prun(O, c)
+        q = _f64(O, c.query, dtype)
+        G = c.spec.num_heads // c.spec.num_kv_heads
+        for s, (K, V) in enumerate(c.pool.contiguous):
+            Kf, Vf = _f64(O, K, dtype), _f64(O, V, dtype)
+            p = int(c.context_lens[s]) - int(c.query_lens[s])
+            for i in range(int(c.query_lens[s])):
+                row = int(c.query_start_loc[s]) + i
+                for h in range(c.spec.num_heads):
+                    ref = _decimal_attention(q[row, h], Kf[h // G, :p + i + 1], Vf[h // G, :p + i + 1],
+                                             c.scale)
+                    assert np.max(np.abs(out[row, h] - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref))), \
+                        (dtype, s, i, h)
+
+
+def pin_prefill_sdpa_causal(O):
+    """A whole prompt prefilled at once (no prefix) equals torch's float64 causal SDPA
+    (``is_causal=True``, torch's own mask) on the contiguous K/V, with GQA."""
+    for i, (dtype, bs, d, Hq, Hkv) in enumerate((("f32", 16, 16, 4, 2), ("bf16", 32, 32, 6, 3),
+                                                  ("f16", 16, 64, 2, 2))):
+        c = _pcase(S=3, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, bs=bs, prefix=(0, 0, 0),
+                   chunk=(1, bs + 3, 2 * bs + 1), seed=50 + i)
+        out = _prun(O, c)
+        q = _f64(O, c.query, dtype)
+        for s, (K, V) in enumerate(c.pool.contiguous):
+            q0, q1 = int(c.query_start_loc[s]), int(c.query_start_loc[s + 1])
+            qt = torch.from_numpy(np.ascontiguousarray(q[q0:q1].transpose(1, 0, 2)))[None]
+            kt = torch.from_numpy(np.ascontiguousarray(_f64(O, K, dtype)))[None]
+            vt = torch.from_numpy(np.ascontiguousarray(_f64(O, V, dtype)))[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt, vt, is_causal=True, scale=float(c.scale), enable_gqa=True)[0]
+            ref = ref.numpy().transpose(1, 0, 2)
+            assert np.max(np.abs(out[q0:q1] - ref)) <= 1e-12, (dtype, s)
+
+
+def pin_prefill_rows_are_decodes(O):
+    """Each prefill row equals a single-query decode of that row's query over the context up
+    to and including its own position (decode_ref is pinned on its own above)."""
+    c = _pcase(S=3, Hq=4, Hkv=1, d=16, dtype="bf16", prefix=(0, 7, 33), chunk=(5, 9, 16), seed=60)
+    out = _prun(O, c)
+    rows, tables, lens = [], [], []
+    for s in range(3):
+        p = int(c.context_lens[s]) - int(c.query_lens[s])
+        for i in range(int(c.query_lens[s])):
+            rows.append(int(c.query_start_loc[s]) + i)
+            tables.append(c.pool.block_tables[s])
+            lens.append(p + i + 1)
+    dec = O.decode_ref(c.query[rows], c.pool.key_cache, c.pool.value_cache,
+                       np.stack(tables), np.array(lens, np.int32), c.block_size, c.scale, c.dtype)
+    assert np.array_equal(out[rows], dec)
+
+
+def pin_prefill_rechunking(O):
+    """Cutting a prompt into chunks changes nothing: prefilling tokens a..b-1 on top of a
+    cached prefix of a tokens reproduces rows a..b-1 of the whole-prompt prefill."""
+    c = _pcase(S=2, Hq=2, Hkv=2, d=16, dtype="f16", prefix=(0, 0), chunk=(40, 23), seed=61)
+    whole = _prun(O, c)
+    for s in range(2):
+        base = int(c.query_start_loc[s])
+        n = int(c.query_lens[s])
+        for cuts in ((0, 1, 17, n), (0, 16, n), (0, n - 1, n)):
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                got = _prun(O, c, query=c.query[base + a:base + b],
+                            block_tables=c.pool.block_tables[s:s + 1],
+                            query_start_loc=np.array([0, b - a], np.int32),
+                            context_lens=np.array([b], np.int32))
+                assert np.array_equal(got, whole[base + a:base + b]), (s, cuts, a, b)
+
+
+def pin_prefill_layout_and_poison(O):
+    """Moving blocks to other physical ids, NaN in unused slots/blocks and junk table entries
+    change nothing; a chunk longer than its context, or an empty chunk, yields zero rows."""
+    spec = W.PrefillSpec("pin", 62, 4, 2, 2, 16, "bf16", 16, ("fixed", [0, 14, 16, 30]),
+                         ("fixed", [1, 2, 16, 3]), max_blocks_per_seq=5)
+    clean = W.build_prefill_case(spec)
+    base = _prun(O, clean)
+    assert np.all(np.isfinite(base))
+    for fill in (-1, 2**31 - 1):
+        dirty = W.build_prefill_case(spec, poison=True, table_fill=fill)
+        assert np.array_equal(_prun(O, dirty), base)
+    NB = clean.pool.num_blocks
+    pi = np.random.default_rng(3).permutation(NB)
+    kc, vc = np.empty_like(clean.pool.key_cache), np.empty_like(clean.pool.value_cache)
+    kc[pi], vc[pi] = clean.pool.key_cache, clean.pool.value_cache
+    bt = np.where(clean.pool.block_tables >= 0, pi[np.clip(clean.pool.block_tables, 0, NB - 1)], -1)
+    assert np.array_equal(_prun(O, clean, key_cache=kc, value_cache=vc,
+                                block_tables=bt.astype(np.int32)), base)
+    lens = clean.context_lens.copy()
+    lens[2] = 15                        # 16-token chunk on a 15-token context: no placement
+    got = _prun(O, clean, context_lens=lens)
+    q0, q1 = int(clean.query_start_loc[2]), int(clean.query_start_loc[3])
+    assert np.all(got[q0:q1] == 0.0)
+    assert np.array_equal(np.delete(got, np.s_[q0:q1], axis=0), np.delete(base, np.s_[q0:q1], axis=0))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

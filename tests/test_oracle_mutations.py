@@ -50,6 +50,15 @@ MUTATIONS = [
      "reserved = sum(lengths)"),
     ("swap writes the source", "        kd[dst] = src_key[src]\n", "        kd[src % nd] = src_key[dst % ns]\n"),
     ("swap bounds use one pool", "if not (0 <= src < ns and 0 <= dst < nd):", "if not (0 <= src < nd and 0 <= dst < nd):"),
+    ("prefill strict causal", "_softmax_weighted_sum(K[kv, :last + 1], V[kv, :last + 1],",
+     "_softmax_weighted_sum(K[kv, :last + 2], V[kv, :last + 2],"),
+    ("prefill excludes itself", "            last = n - L + i ", "            last = n - L + i - 1 "),
+    ("prefill ignores cached prefix", "            last = n - L + i ", "            last = i "),
+    ("prefill sees whole chunk", "            last = n - L + i ", "            last = n - 1 "),
+    ("prefill GQA map", "                kv = h // G\n                out[q0 + i, h]",
+     "                kv = h % Hkv\n                out[q0 + i, h]"),
+    ("prefill row offset", "q = storage_to_f64(query[q0:q1], dtype)", "q = storage_to_f64(query[0:L], dtype)"),
+    ("prefill no length guard", "if L <= 0 or n < L:", "if L <= 0:"),
 ]
 
 
