@@ -235,6 +235,41 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          pa_dtype dtype, void* stream);
 
+/*
+ * pa_prefill — causal attention of a chunk of new tokens per sequence over the paged cache
+ * (prefill, or one chunk of a chunked prefill).
+ *
+ * Prefill is the compute-heavy phase before decoding (xasun.com summary §三, compute-pattern
+ * row), and a long prompt may be prefilled in chunks (the chunked-prefill switch in the vLLM
+ * example on the jsqmd.com page).  Sequence s owns query rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1 (L_s rows, L_s <= max_query_len).  Its
+ * n = context_lens[s] cached tokens already include the chunk's own K/V (call
+ * pa_reshape_and_cache for the chunk first), so chunk token i sits at position n - L_s + i:
+ *   out[row][h] = sum_{t <= n-L_s+i} softmax_t(scale * <query[row][h], K_s[t][h/G]>) V_s[t][h/G]
+ * with K_s/V_s read through block_tables as in pa_decode and G = num_heads / num_kv_heads.
+ *
+ *   out, query     [T][num_heads][head_dim] dtype, T = query_start_loc[num_seqs]
+ *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim] dtype
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]
+ *   query_start_loc  int32 [num_seqs + 1], non-decreasing, query_start_loc[0] = 0
+ *   context_lens   int32 [num_seqs]
+ * Rows of a sequence with L_s > n, or n > max_blocks_per_seq * block_size, are written as
+ * zeros; rows past max_query_len of a longer chunk are not written.  Only the first
+ * ceil(n / block_size) table entries and the first n slots are read.
+ * Supported: dtype f16 or bf16, head_dim 128, block_size 16 or 32.  Arithmetic: 16-bit
+ * operands on the matrix cores with fp32 accumulation; the softmax probabilities keep about
+ * 16 significant bits for bf16 (two products) and 11 for f16, unless flags has
+ * PA_PREFILL_BF16_P, which rounds bf16 probabilities to bfloat16 once (one product, faster,
+ * about 8 bits).  No workspace; nothing is allocated.
+ */
+#define PA_PREFILL_BF16_P 0x1u
+pa_status pa_prefill(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* query_start_loc,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                     float scale, pa_dtype dtype, uint32_t flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -313,4 +313,52 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_prefill(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* query_start_loc,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                     float scale, pa_dtype dtype, uint32_t flags, void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, 0);
+  if (st != PA_OK) return st;
+  if (max_query_len < 0) return PA_ERR_BAD_SHAPE;
+  if (dt == DT::F32 || head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if ((flags & ~PA_PREFILL_BF16_P) != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
+      !context_lens)
+    return PA_ERR_NULL_PTR;
+  if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  const int G = num_heads / num_kv_heads;
+  const long row_tiles = ((long)max_query_len * G + 127) / 128;
+  const long grid = (long)num_seqs * num_kv_heads * row_tiles;
+  if (grid > 0x7FFFFFFFL || (long)max_query_len * G > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
+
+  pa::PrefillParams p;
+  p.out = out;
+  p.q = query;
+  p.kc = key_cache;
+  p.vc = value_cache;
+  p.block_tables = block_tables;
+  p.query_start_loc = query_start_loc;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = G;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.max_query_len = max_query_len;
+  p.row_tiles = (int)row_tiles;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const bool split_p = !(dt == DT::BF16 && (flags & PA_PREFILL_BF16_P));
+  (void)hipGetLastError();
+  return launch_status(pa::launch_prefill_mfma(dt, block_size, split_p, p, (int)grid,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

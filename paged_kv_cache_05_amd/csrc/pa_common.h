@@ -143,6 +143,18 @@ __device__ __forceinline__ uint4 load_kv(const void* ptr) {
   else return *reinterpret_cast<const uint4*>(ptr);
 }
 
+// Column e (0..7) of a 4x8 tile of 16-bit values held as 4 rows r[j] (row j = token j, word q
+// = dims 2q, 2q+1): the 4 tokens' values of dim e, two per word, token order preserved.
+__device__ __forceinline__ uint2 tile_column(const uint4 (&r)[4], int e) {
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  auto word = [&](const uint4& v) -> uint32_t {
+    const int q = e >> 1;
+    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+  };
+  return make_uint2(__builtin_amdgcn_perm(word(r[1]), word(r[0]), sel),
+                    __builtin_amdgcn_perm(word(r[3]), word(r[2]), sel));
+}
+
 // Softmax running state uses base-2 exponents: scores are pre-multiplied by log2(e).
 // A running max of -inf means "no token seen"; exp2(x - safe(m)) is then 0 for every x
 // that is itself -inf and the state stays empty.
@@ -176,11 +188,27 @@ struct MergeParams {
   int32_t num_seqs, num_heads, max_blocks_per_seq, block_size, partition, max_parts;
 };
 
+struct PrefillParams {
+  void* out;                        // [T][Hq][D]
+  const void* q;                    // [T][Hq][D]
+  const void* kc;
+  const void* vc;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;   // [S + 1]
+  const int32_t* context_lens;      // [S], the chunk included
+  int32_t num_seqs, num_heads, num_kv_heads, group;
+  int32_t max_blocks_per_seq, num_blocks, max_query_len;
+  int32_t row_tiles;                // workgroups per (sequence, KV head): ceil(max_query_len * G / 128)
+  float scale_log2;
+};
+
 // host-side launchers (return hipSuccess or the launch error)
 hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
                               bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
                               bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const PrefillParams& p,
+                              int grid, hipStream_t st);
 hipError_t launch_merge(DT dt, int head_dim, const MergeParams& p, hipStream_t st);
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int64_t* slots, int num_tokens, int row_vecs,

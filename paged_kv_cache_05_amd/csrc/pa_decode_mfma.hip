@@ -63,18 +63,6 @@ template <> struct Mfma<DT::F16> {
   }
 };
 
-// Column e (0..7) of a 4x8 tile of 16-bit values held as 4 rows r[j] (row j = token j, word q
-// = dims 2q, 2q+1): the 4 tokens' values of dim e, two per word, token order preserved.
-__device__ __forceinline__ uint2 tile_column(const uint4 (&r)[4], int e) {
-  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-  auto word = [&](const uint4& v) -> uint32_t {
-    const int q = e >> 1;
-    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
-  };
-  return make_uint2(__builtin_amdgcn_perm(word(r[1]), word(r[0]), sel),
-                    __builtin_amdgcn_perm(word(r[3]), word(r[2]), sel));
-}
-
 template <DT dt, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int D = 128;

@@ -1,0 +1,339 @@
+// Paged prefill attention on the matrix cores (gfx950): causal attention of a chunk of new
+// tokens per sequence over the paged KV cache.
+//
+// Prefill is the compute-heavy phase before decoding (UltraLAB summary of Kwon et al.
+// (xasun.com) §三, table row on the compute pattern), and serving engines may cut a long prompt
+// into chunks (the chunked-prefill switch in the vLLM example on the PyTorch-CUDA-v2.9
+// PagedAttention page, jsqmd.com).  Sequence s contributes L query rows; its n cached tokens
+// already hold the chunk's own K/V (reshape_and_cache runs first), so chunk token i sits at
+// position n - L + i and attends to positions 0 .. n - L + i, read block by block through the
+// block table exactly as decode reads them.
+//
+// Work decomposition.  A workgroup (4 waves) owns 128 query rows of one (sequence, KV head):
+// row r is chunk token r / G with query head kvh*G + r % G, so the G heads sharing a KV head
+// share every K/V tile.  Each wave owns 32 rows.  Keys/values stream through LDS in tiles of
+// 64 tokens, double-buffered: while the waves multiply tile k, every thread has tile k+1's
+// loads in flight (four 16-byte rows of K and of V per thread) and stores them after its
+// products.  One barrier per tile.
+//
+// Products, per wave and tile (v_mfma_f32_16x16x32, 16-bit operands, fp32 accumulation):
+//   S^T[64 tokens x 32 rows] = K[64 x 128] Q^T[128 x 32]: 4 token blocks x 2 row blocks x 4
+//     depth steps = 32 MFMAs.  A (K): lane l reads K[token 16j + l%16][dims 32c + 8(l/16) ..
+//     +8] from LDS; B (Q^T): the wave's queries, held in registers for the whole loop.  Result:
+//     lane l holds row 16n + l%16 at tokens 16j + 4(l/16) .. +4.
+//   O^T[128 dims x 32 rows] += V^T[128 x 64] P^T[64 x 32]: 2 token halves x 8 dim blocks x 2
+//     row blocks = 32 MFMAs.  The B operand (P^T) of lane l must be row l%16 at 8 tokens, which
+//     are exactly 8 of the scores the lane already holds (tokens 4(l/16)+i of blocks 2h and
+//     2h+1): the reduction order inside one MFMA is free, so P never moves between lanes.  The
+//     A operand (V^T) needs 8 tokens of one dim per lane, so V is stored transposed in LDS, with
+//     each dim row's tokens in the same order, making every A operand one 16-byte LDS read.
+//   O^T keeps each query row in one lane column, so the softmax rescale of a row touches only
+//   lanes that already hold that row's running max (no cross-lane traffic).
+// With bfloat16 data, P is split into a 16-bit high part and remainder (two MFMAs per O^T
+// product) so the probabilities keep about 16 significant bits; fp16 P keeps 11 bits in one.
+//
+// LDS layouts (16-byte chunks, swizzled so that the 8 lanes served per LDS cycle hit distinct
+// banks on both the stores and the MFMA operand reads):
+//   K tile  [64 tokens][16 chunks of 8 dims], chunk c of token t at slot c ^ (t & 15).
+//   V^T tile [128 dims][8 chunks of 8 token positions], chunk c of dim d at c ^ swz(d).
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <DT dt> struct Mma;
+template <> struct Mma<DT::BF16> {
+  __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
+  __device__ __forceinline__ static float value(uint32_t b) { return __uint_as_float(b << 16); }
+};
+template <> struct Mma<DT::F16> {
+  __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
+  __device__ __forceinline__ static float value(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  }
+};
+
+constexpr int kD = 128;          // head dim
+constexpr int kRow = kD * 2;     // bytes per token row
+constexpr int kTile = 64;        // KV tokens per LDS tile
+constexpr int kRowsWave = 32;    // query rows per wave
+constexpr int kRowsWG = 128;     // query rows per workgroup
+
+__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+
+template <DT dt, int BS, bool SPLIT_P>
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParams p) {
+  using M = Mma<dt>;
+  static_assert(BS % 16 == 0, "a thread's 4 tokens must sit in one block");
+  __shared__ uint4 s_k[2][kTile * 16];
+  __shared__ uint4 s_v[2][kD * 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (id mod 8); renumbering gives
+  // each XCD a contiguous range of items, so the row tiles of one (sequence, KV head), which
+  // read the same K/V, share that XCD's L2.  Within a unit the last rows (longest causal
+  // range) come first.
+  const int total = p.num_seqs * p.num_kv_heads * p.row_tiles;
+  int w = blockIdx.x;
+  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
+  const int unit = w / p.row_tiles;
+  const int rt = p.row_tiles - 1 - (w - unit * p.row_tiles);
+  const int kvh = unit % p.num_kv_heads;
+  const int s = unit / p.num_kv_heads;
+
+  const int q0 = p.query_start_loc[s];
+  const int L_all = p.query_start_loc[s + 1] - q0;  // chunk length (sets the positions)
+  const int L = min(L_all, p.max_query_len);        // rows this grid covers
+  const int n = p.context_lens[s];
+  const int G = p.group;
+  const int rows = L * G;
+  const int row0 = rt * kRowsWG;
+  if (L <= 0 || row0 >= rows) return;
+
+  // element offset of row r's query / output vector
+  auto row_off = [&](int r) -> size_t {
+    const int t = r / G;
+    return ((size_t)(q0 + t) * p.num_heads + kvh * G + (r - t * G)) * kD;
+  };
+
+  if (n < L_all || n > p.max_blocks_per_seq * BS) {  // the chunk does not fit its context: zeros
+    for (int idx = tid; idx < kRowsWG * 16; idx += 256) {
+      const int r = row0 + (idx >> 4);
+      if (r < rows)
+        *reinterpret_cast<uint4*>((char*)p.out + row_off(r) * 2 + (idx & 15) * 16) =
+            make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+
+  const int prefix = n - L_all;
+  const int last_row = min(rows, row0 + kRowsWG) - 1;
+  const int ntiles = (prefix + last_row / G + 1 + kTile - 1) / kTile;
+
+  const int wrow0 = row0 + wave * kRowsWave;
+  const bool wave_active = wrow0 < rows;
+  const int w_kv_end = wave_active ? prefix + (min(rows, wrow0 + kRowsWave) - 1) / G + 1 : 0;
+  const int w_kv_min = prefix + wrow0 / G;  // no row of the wave stops before this position
+
+  // Q^T operand of the wave (16-bit values as stored) and the last position each of the
+  // lane's two rows may attend to.  Rows past the chunk reuse the last row (never stored).
+  uint4 qb[2][4];
+  int lim[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const int r = wrow0 + 16 * c2 + lr;
+    const int rc = min(r, rows - 1);
+    lim[c2] = prefix + rc / G;
+    const char* qp = (const char*)p.q + row_off(rc) * 2;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qb[c2][c] = r < rows ? *reinterpret_cast<const uint4*>(qp + (32 * c + 8 * lg) * 2)
+                           : make_uint4(0, 0, 0, 0);
+  }
+
+  // Loader role: thread (tg, dc) moves tokens 4tg .. 4tg+3 of a tile, dims 8dc .. 8dc+7.
+  const int tg = tid >> 4, dc = tid & 15;
+  const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const int nb_live = (n + BS - 1) / BS;
+  const size_t head_off = (size_t)kvh * BS * kRow;
+  const size_t blk_stride = (size_t)p.num_kv_heads * BS * kRow;
+  auto entry = [&](int tile) -> int {
+    const int page = (tile * kTile + 4 * tg) / BS;
+    return (tile < ntiles && page < nb_live) ? table[page] : -1;
+  };
+  uint4 kr[4], vr[4];
+  auto issue = [&](int tile, int ent) {
+    const int t0 = tile * kTile + 4 * tg;
+    const bool ok = ent >= 0 && ent < p.num_blocks;
+    const size_t off = (size_t)(ok ? ent : 0) * blk_stride + head_off +
+                       (size_t)(t0 % BS) * kRow + dc * 16;
+    const char* kp = (const char*)p.kc + off;
+    const char* vp = (const char*)p.vc + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool live = ok && t0 + i < n;   // slots past the context are never read
+      kr[i] = live ? *reinterpret_cast<const uint4*>(kp + i * kRow) : make_uint4(0, 0, 0, 0);
+      vr[i] = live ? *reinterpret_cast<const uint4*>(vp + i * kRow) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // V^T position of this thread's tokens: token 32h + 16b + 4g + i sits at 32h + 8g + 4b + i,
+  // so the 8 tokens one MFMA lane needs (4g+i of 16-token blocks 2h and 2h+1) are contiguous.
+  const int v_chunk = 4 * (tg >> 3) + (tg & 3);
+  const int v_half = (tg >> 2) & 1;
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * tg + i;
+      s_k[buf][t * 16 + (dc ^ (t & 15))] = kr[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * dc + e;
+      char* dst = reinterpret_cast<char*>(&s_v[buf][d * 8 + (v_chunk ^ vswz(d))]) + 8 * v_half;
+      *reinterpret_cast<uint2*>(dst) = tile_column(vr, e);
+    }
+  };
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][0] = o[dt2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max of each row (log2 units)
+  float l_run[2] = {0.f, 0.f};              // this lane's share of each row's denominator
+
+  int ent_next = entry(1);
+  issue(0, entry(0));
+  stash(0);
+  __syncthreads();
+
+  for (int k = 0; k < ntiles; ++k) {
+    const int buf = k & 1;
+    const bool more = k + 1 < ntiles;
+    const int ent_after = entry(k + 2);
+    if (more) issue(k + 1, ent_next);
+
+    // The tile is consumed in two 32-token halves, each a complete online-softmax step
+    // (scores, max, rescale, probabilities, products), which keeps half as many scores live.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tstart = k * kTile + 32 * h;
+      if (!(wave_active && tstart < w_kv_end)) continue;   // wave-uniform
+      f32x4 st[2][2];   // [16-token block][row block]
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int j = 2 * h + jb;
+        st[jb][0] = st[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 a = s_k[buf][(16 * j + lr) * 16 + ((4 * c + lg) ^ lr)];
+          st[jb][0] = M::mma(a, qb[0][c], st[jb][0]);
+          st[jb][1] = M::mma(a, qb[1][c], st[jb][1]);
+        }
+      }
+      // scale, causal mask (only where the half reaches past some row's last position), max
+      const bool mask = tstart + 31 > w_kv_min;
+      float mx[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        mx[c2] = -INFINITY;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = st[jb][c2][i] * p.scale_log2;
+            if (mask && tstart + 16 * jb + 4 * lg + i > lim[c2]) x = -INFINITY;
+            st[jb][c2][i] = x;
+            mx[c2] = fmaxf(mx[c2], x);
+          }
+        mx[c2] = fmaxf(mx[c2], __shfl_xor(mx[c2], 16));
+        mx[c2] = fmaxf(mx[c2], __shfl_xor(mx[c2], 32));
+      }
+      // Position 0 is in the first half every row sees, so m_run is finite from then on and a
+      // row masked out of a later half keeps its max (alpha = 1).
+      uint4 ph[2], pl[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const float m_new = fmaxf(m_run[c2], mx[c2]);
+        const float alpha = fast_exp2(m_run[c2] - m_new);
+        m_run[c2] = m_new;
+#pragma unroll
+        for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][c2] *= alpha;
+        float sum = 0.f;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float rem[2];
+          uint32_t hb[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float pv = fast_exp2(st[(e + u) >> 2][c2][(e + u) & 3] - m_new);
+            sum += pv;
+            hb[u] = M::bits(pv);
+            rem[u] = pv - M::value(hb[u]);
+          }
+          hw[e >> 1] = hb[0] | (hb[1] << 16);
+          if constexpr (SPLIT_P) lw[e >> 1] = M::bits(rem[0]) | (M::bits(rem[1]) << 16);
+        }
+        ph[c2] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        if constexpr (SPLIT_P) pl[c2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        l_run[c2] = fmaf(l_run[c2], alpha, sum);
+      }
+#pragma unroll
+      for (int dt2 = 0; dt2 < 8; ++dt2) {
+        const int d = 16 * dt2 + lr;
+        const uint4 a = s_v[buf][d * 8 + ((4 * h + lg) ^ vswz(d))];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, ph[c2], o[dt2][c2]);
+        if constexpr (SPLIT_P) {
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, pl[c2], o[dt2][c2]);
+        }
+      }
+    }
+
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    ent_next = ent_after;
+  }
+
+  if (!wave_active) return;
+  // Finalise: the four lanes holding a row add their denominators; lane l writes dims
+  // 16b + 4(l/16) .. +4 of its rows.
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    float l = l_run[c2];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = 1.0f / l;
+    const int r = wrow0 + 16 * c2 + lr;
+    if (r < rows) {
+      char* op = (char*)p.out + row_off(r) * 2;
+#pragma unroll
+      for (int dt2 = 0; dt2 < 8; ++dt2) {
+        const f32x4 v = o[dt2][c2];
+        const uint2 w2 = make_uint2(M::bits(v[0] * inv) | (M::bits(v[1] * inv) << 16),
+                                    M::bits(v[2] * inv) | (M::bits(v[3] * inv) << 16));
+        *reinterpret_cast<uint2*>(op + (16 * dt2 + 4 * lg) * 2) = w2;
+      }
+    }
+  }
+}
+
+template <DT dt, int BS, bool SPLIT>
+hipError_t go(const PrefillParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_mfma_kernel<dt, BS, SPLIT>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const PrefillParams& p,
+                               int grid, hipStream_t st) {
+  if (dt == DT::BF16) {
+    if (!split_p) return block_size == 16 ? go<DT::BF16, 16, false>(p, grid, st)
+                                          : go<DT::BF16, 32, false>(p, grid, st);
+    return block_size == 16 ? go<DT::BF16, 16, true>(p, grid, st)
+                            : go<DT::BF16, 32, true>(p, grid, st);
+  }
+  if (dt == DT::F16)
+    return block_size == 16 ? go<DT::F16, 16, false>(p, grid, st)
+                            : go<DT::F16, 32, false>(p, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -45,6 +45,7 @@ _SIGNATURES = {
     "pa_reshape_and_cache": (_c_int, [_p] * 5 + [_c_int] * 6 + [_p]),
     "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
     "pa_swap_blocks": (_c_int, [_p, _p, _c_int, _p, _p, _c_int, _p] + [_c_int] * 5 + [_p]),
+    "pa_prefill": (_c_int, [_p] * 7 + [_c_int] * 8 + [_c_float, _c_int, ctypes.c_uint32, _p]),
 }
 
 
@@ -254,3 +255,38 @@ def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, *, stream
     _check(load().pa_swap_blocks(_ptr(src_key), _ptr(src_value), NS, _ptr(dst_key), _ptr(dst_value),
                                  ND, _ptr(block_mapping), block_mapping.shape[0], Hkv, D, BS,
                                  _dtype_code(src_key), _stream(dev, stream)), "pa_swap_blocks")
+
+
+PA_PREFILL_BF16_P = 0x1
+
+
+def prefill(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens, scale,
+            max_query_len, *, bf16_p=False, stream=None):
+    """pa_prefill: causal attention of each sequence's chunk of new tokens over the paged cache.
+
+    ``query``/``out`` [T, Hq, d] hold the chunks back to back; sequence s owns rows
+    ``query_start_loc[s] .. query_start_loc[s+1]-1`` (int32 [S+1]); ``context_lens`` (int32 [S])
+    counts the cached tokens including the chunk.  ``max_query_len`` is a host integer no
+    smaller than any chunk.  ``bf16_p`` sets PA_PREFILL_BF16_P."""
+    import torch
+    dev = _dev(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens)
+    T, Hq, D = query.shape
+    NB, Hkv, BS, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or D2 != D:
+        raise ValueError("key_cache/value_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must have the query's shape")
+    if not (out.dtype == query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("out, query and both pools must share one element type")
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start_loc.dtype != torch.int32):
+        raise TypeError("block_tables, query_start_loc and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start_loc.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and query_start_loc [S + 1]")
+    _check(load().pa_prefill(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                             _ptr(block_tables), _ptr(query_start_loc), _ptr(context_lens), S, Hq,
+                             Hkv, D, BS, NB, block_tables.shape[1], int(max_query_len),
+                             float(scale), _dtype_code(query),
+                             PA_PREFILL_BF16_P if bf16_p else 0, _stream(dev, stream)), "pa_prefill")
+    return out

@@ -114,3 +114,29 @@ def test_swap_blocks_argument_errors(lib):
     assert lib.pa_swap_blocks(p, p, -1, p, p, 4, p, 2, 2, 64, 16, 0, None) == 2
     assert lib.pa_swap_blocks(p, p, 4, p, p, 4, p, 2, 1, 3, 1, 1, None) == 3     # 6-byte blocks
     assert lib.pa_swap_blocks(None, None, 4, None, None, 4, None, 0, 2, 64, 16, 0, None) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(out=1, q=1, kc=1, vc=1, bt=1, qsl=1, cl=1, S=4, Hq=8, Hkv=2, D=128, BS=16, NB=100,
+             maxb=8, maxq=64, scale=0.1, dtype=2, flags=0)
+    a.update(kw)
+    p = lambda v: ctypes.c_void_p(v) if v else None
+    return lib.pa_prefill(p(a["out"]), p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), p(a["qsl"]),
+                          p(a["cl"]), a["S"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"],
+                          a["maxb"], a["maxq"], a["scale"], a["dtype"], a["flags"], None)
+
+
+def test_prefill_argument_errors(lib):
+    assert _prefill(lib, qsl=0) == 1                 # PA_ERR_NULL_PTR
+    assert _prefill(lib, out=0) == 1
+    assert _prefill(lib, Hq=6, Hkv=4) == 2           # PA_ERR_BAD_SHAPE
+    assert _prefill(lib, maxq=-1) == 2
+    assert _prefill(lib, NB=0) == 2
+    assert _prefill(lib, scale=float("inf")) == 2
+    assert _prefill(lib, dtype=0) == 3               # PA_ERR_UNSUPPORTED: f32
+    assert _prefill(lib, D=64) == 3
+    assert _prefill(lib, BS=8) == 3
+    assert _prefill(lib, flags=0x2) == 3
+    assert _prefill(lib, flags=0x1, out=0) == 1      # the bf16-probabilities flag is accepted
+    assert _prefill(lib, S=0, out=0) == 0            # nothing to do
+    assert _prefill(lib, maxq=0, out=0) == 0
