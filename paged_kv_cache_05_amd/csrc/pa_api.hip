@@ -354,7 +354,11 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache, const 
   p.num_blocks = num_blocks;
   p.max_query_len = max_query_len;
   p.row_tiles = (int)row_tiles;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  // The kernel takes the row max on raw scores, which needs a positive multiplier: a negative
+  // scale flips the query signs instead (exact), and 0 becomes the smallest normal float
+  // (every score then rounds to a zero exponent, as scale 0 requires).
+  p.scale_log2 = std::max(std::fabs(scale) * 1.4426950408889634f, 1.17549435e-38f);
+  p.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
   const bool split_p = !(dt == DT::BF16 && (flags & PA_PREFILL_BF16_P));
   (void)hipGetLastError();
   return launch_status(pa::launch_prefill_mfma(dt, block_size, split_p, p, (int)grid,

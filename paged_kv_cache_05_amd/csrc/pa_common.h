@@ -199,7 +199,8 @@ struct PrefillParams {
   int32_t num_seqs, num_heads, num_kv_heads, group;
   int32_t max_blocks_per_seq, num_blocks, max_query_len;
   int32_t row_tiles;                // workgroups per (sequence, KV head): ceil(max_query_len * G / 128)
-  float scale_log2;
+  float scale_log2;                 // |scale| * log2(e), at least FLT_MIN (so it is > 0)
+  uint32_t q_sign;                  // 0x80008000 when scale < 0: query signs are flipped instead
 };
 
 // host-side launchers (return hipSuccess or the launch error)

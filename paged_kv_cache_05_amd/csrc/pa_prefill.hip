@@ -44,6 +44,9 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <DT dt> struct Mma;
 template <> struct Mma<DT::BF16> {
@@ -52,7 +55,10 @@ template <> struct Mma<DT::BF16> {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
   __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
-  __device__ __forceinline__ static float value(uint32_t b) { return __uint_as_float(b << 16); }
+  // two values, nearest-even, in one v_cvt_pk_bf16_f32
+  __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  }
 };
 template <> struct Mma<DT::F16> {
   __device__ __forceinline__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
@@ -60,8 +66,8 @@ template <> struct Mma<DT::F16> {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
   __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
-  __device__ __forceinline__ static float value(uint32_t b) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
   }
 };
 
@@ -70,6 +76,7 @@ constexpr int kRow = kD * 2;     // bytes per token row
 constexpr int kTile = 64;        // KV tokens per LDS tile
 constexpr int kRowsWave = 32;    // query rows per wave
 constexpr int kRowsWG = 128;     // query rows per workgroup
+constexpr float kLazy = 8.0f;    // running-max slack (log2 units): probabilities < 256
 
 __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
@@ -145,6 +152,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
     for (int c = 0; c < 4; ++c)
       qb[c2][c] = r < rows ? *reinterpret_cast<const uint4*>(qp + (32 * c + 8 * lg) * 2)
                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qb[c2][c].x ^= p.q_sign;
+      qb[c2][c].y ^= p.q_sign;
+      qb[c2][c].z ^= p.q_sign;
+      qb[c2][c].w ^= p.q_sign;
+    }
   }
 
   // Loader role: thread (tg, dc) moves tokens 4tg .. 4tg+3 of a tile, dims 8dc .. 8dc+7.
@@ -225,8 +239,20 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
           st[jb][1] = M::mma(a, qb[1][c], st[jb][1]);
         }
       }
-      // scale, causal mask (only where the half reaches past some row's last position), max
-      const bool mask = tstart + 31 > w_kv_min;
+      // Causal mask (only where the half reaches past some row's last position) and the row
+      // max, both on the raw scores: scale > 0, so the max commutes with it.  The masking
+      // branch holds a scheduling barrier so that it stays a branch (halves every row sees
+      // in full then carry no per-score compare).
+      if (tstart + 31 > w_kv_min) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tstart + 16 * jb + 4 * lg + i > lim[c2]) st[jb][c2][i] = -INFINITY;
+      }
       float mx[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -234,44 +260,56 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = st[jb][c2][i] * p.scale_log2;
-            if (mask && tstart + 16 * jb + 4 * lg + i > lim[c2]) x = -INFINITY;
-            st[jb][c2][i] = x;
-            mx[c2] = fmaxf(mx[c2], x);
-          }
+          for (int i = 0; i < 4; ++i) mx[c2] = fmaxf(mx[c2], st[jb][c2][i]);
         mx[c2] = fmaxf(mx[c2], __shfl_xor(mx[c2], 16));
         mx[c2] = fmaxf(mx[c2], __shfl_xor(mx[c2], 32));
       }
-      // Position 0 is in the first half every row sees, so m_run is finite from then on and a
-      // row masked out of a later half keeps its max (alpha = 1).
+      // Lazy running max (log2 units): the reference point moves only when a row's max
+      // exceeds it by more than kLazy, so probabilities stay below 2^kLazy and the O/l rescale
+      // (64 multiplies per lane) runs only on the few steps where some row's max jumps.  Any
+      // reference point gives the same o / l; position 0, in every row's first half, makes
+      // the first step always move it from -inf.
+      bool grow[2];
+      float m_new[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const float ms = mx[c2] == -INFINITY ? -INFINITY : mx[c2] * p.scale_log2;
+        grow[c2] = ms > m_run[c2] + kLazy;
+        m_new[c2] = grow[c2] ? ms : m_run[c2];
+      }
+      if (__any(grow[0] || grow[1])) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const float alpha = grow[c2] ? fast_exp2(m_run[c2] - m_new[c2]) : 1.0f;
+          m_run[c2] = m_new[c2];
+          l_run[c2] *= alpha;
+#pragma unroll
+          for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][c2] *= alpha;
+        }
+      }
+      // Probabilities exp2(s * scale_log2 - m) with one FMA each, packed as the B operand.
       uint4 ph[2], pl[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const float m_new = fmaxf(m_run[c2], mx[c2]);
-        const float alpha = fast_exp2(m_run[c2] - m_new);
-        m_run[c2] = m_new;
+        const float neg_m = -m_run[c2];
+        float pv[8];
 #pragma unroll
-        for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][c2] *= alpha;
-        float sum = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = fast_exp2(fmaf(st[e >> 2][c2][e & 3], p.scale_log2, neg_m));
+          l_run[c2] += pv[e];
+        }
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          float rem[2];
-          uint32_t hb[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float pv = fast_exp2(st[(e + u) >> 2][c2][(e + u) & 3] - m_new);
-            sum += pv;
-            hb[u] = M::bits(pv);
-            rem[u] = pv - M::value(hb[u]);
+          hw[e >> 1] = M::pack2(pv[e], pv[e + 1]);
+          if constexpr (SPLIT_P) {
+            const float r0 = pv[e] - __uint_as_float(hw[e >> 1] << 16);
+            const float r1 = pv[e + 1] - __uint_as_float(hw[e >> 1] & 0xFFFF0000u);
+            lw[e >> 1] = M::pack2(r0, r1);
           }
-          hw[e >> 1] = hb[0] | (hb[1] << 16);
-          if constexpr (SPLIT_P) lw[e >> 1] = M::bits(rem[0]) | (M::bits(rem[1]) << 16);
         }
         ph[c2] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         if constexpr (SPLIT_P) pl[c2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        l_run[c2] = fmaf(l_run[c2], alpha, sum);
       }
 #pragma unroll
       for (int dt2 = 0; dt2 < 8; ++dt2) {
