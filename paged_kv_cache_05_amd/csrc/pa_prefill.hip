@@ -54,6 +54,7 @@ template <> struct Mma<DT::BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  static constexpr uint32_t kOnes = 0x3F803F80u;   // two bfloat16 ones
   __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
   // two values, nearest-even, in one v_cvt_pk_bf16_f32
   __device__ __forceinline__ static uint32_t pack2(float a, float b) {
@@ -65,6 +66,7 @@ template <> struct Mma<DT::F16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  static constexpr uint32_t kOnes = 0x3C003C00u;   // two fp16 ones
   __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
   __device__ __forceinline__ static uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
@@ -79,6 +81,18 @@ constexpr int kRowsWG = 128;     // query rows per workgroup
 constexpr float kLazy = 8.0f;    // running-max slack (log2 units): probabilities < 256
 
 __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+
+// Max over the four lanes l, l^16, l^32, l^48 (one query row of an MFMA output).  Each
+// permlane swap leaves, in every lane, its own value and its partner's (lane ^ 32, then
+// lane ^ 16) in the two results, whichever result holds which.
+__device__ __forceinline__ float row_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <DT dt, int BS, bool SPLIT_P>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParams p) {
@@ -174,16 +188,25 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   uint4 kr[4], vr[4];
   auto issue = [&](int tile, int ent) {
     const int t0 = tile * kTile + 4 * tg;
-    const bool ok = ent >= 0 && ent < p.num_blocks;
-    const size_t off = (size_t)(ok ? ent : 0) * blk_stride + head_off +
-                       (size_t)(t0 % BS) * kRow + dc * 16;
+    // An id outside the pool (a broken table) is replaced by block 0, so no access leaves the
+    // pools; slots past the context are never read.
+    const size_t off = (size_t)((unsigned)ent < (unsigned)p.num_blocks ? ent : 0) * blk_stride +
+                       head_off + (size_t)(t0 % BS) * kRow + dc * 16;
     const char* kp = (const char*)p.kc + off;
     const char* vp = (const char*)p.vc + off;
+    if (t0 + 3 < n) {   // the usual case: four live rows, unconditional loads
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool live = ok && t0 + i < n;   // slots past the context are never read
-      kr[i] = live ? *reinterpret_cast<const uint4*>(kp + i * kRow) : make_uint4(0, 0, 0, 0);
-      vr[i] = live ? *reinterpret_cast<const uint4*>(vp + i * kRow) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        kr[i] = *reinterpret_cast<const uint4*>(kp + i * kRow);
+        vr[i] = *reinterpret_cast<const uint4*>(vp + i * kRow);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool live = t0 + i < n;
+        kr[i] = live ? *reinterpret_cast<const uint4*>(kp + i * kRow) : make_uint4(0, 0, 0, 0);
+        vr[i] = live ? *reinterpret_cast<const uint4*>(vp + i * kRow) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   // V^T position of this thread's tokens: token 32h + 16b + 4g + i sits at 32h + 8g + 4b + i,
@@ -208,7 +231,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 #pragma unroll
   for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][0] = o[dt2][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};  // running max of each row (log2 units)
-  float l_run[2] = {0.f, 0.f};              // this lane's share of each row's denominator
+  // Denominators on the matrix cores: ones^T P^T adds each row's probabilities exactly as
+  // they enter O (16-bit parts included); every element of l_acc[c2] holds the row's sum.
+  f32x4 l_acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const uint4 ones = make_uint4(M::kOnes, M::kOnes, M::kOnes, M::kOnes);
 
   int ent_next = entry(1);
   issue(0, entry(0));
@@ -261,8 +287,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx[c2] = fmaxf(mx[c2], st[jb][c2][i]);
-        mx[c2] = fmaxf(mx[c2], __shfl_xor(mx[c2], 16));
-        mx[c2] = fmaxf(mx[c2], __shfl_xor(mx[c2], 32));
+        mx[c2] = row_max4(mx[c2]);
       }
       // Lazy running max (log2 units): the reference point moves only when a row's max
       // exceeds it by more than kLazy, so probabilities stay below 2^kLazy and the O/l rescale
@@ -282,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
         for (int c2 = 0; c2 < 2; ++c2) {
           const float alpha = grow[c2] ? fast_exp2(m_run[c2] - m_new[c2]) : 1.0f;
           m_run[c2] = m_new[c2];
-          l_run[c2] *= alpha;
+          l_acc[c2] *= alpha;
 #pragma unroll
           for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][c2] *= alpha;
         }
@@ -294,10 +319,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
         const float neg_m = -m_run[c2];
         float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 8; ++e)
           pv[e] = fast_exp2(fmaf(st[e >> 2][c2][e & 3], p.scale_log2, neg_m));
-          l_run[c2] += pv[e];
-        }
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -309,7 +332,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
           }
         }
         ph[c2] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        if constexpr (SPLIT_P) pl[c2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        l_acc[c2] = M::mma(ones, ph[c2], l_acc[c2]);
+        if constexpr (SPLIT_P) {
+          pl[c2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+          l_acc[c2] = M::mma(ones, pl[c2], l_acc[c2]);
+        }
       }
 #pragma unroll
       for (int dt2 = 0; dt2 < 8; ++dt2) {
@@ -334,10 +361,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   // 16b + 4(l/16) .. +4 of its rows.
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    float l = l_run[c2];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / l_acc[c2][0];
     const int r = wrow0 + 16 * c2 + lr;
     if (r < rows) {
       char* op = (char*)p.out + row_off(r) * 2;
