@@ -10,8 +10,10 @@ kernel + log-sum-exp merge).  Inputs are seeded synthetic data drawn on the GPU 
 The reported value is the step's algorithmic bytes divided by the step time (GB/s).  The
 `roofline` object covers the dominant kernel (the decode partition kernel), timed with HIP
 events on the stream it runs on; `cpu_baseline` times the float64 CPU oracle on a bounded
-sample of the same workload.  `--calibrate-copy` instead times copy_blocks on a known number
-of bytes (the reference copy used to scale hardware byte counters).
+sample of the same workload.  `detail` adds the other decode workloads, swap_blocks over the
+host link and pa_prefill on two chunked-prefill workloads (matrix-core bound: TFLOP/s against
+the 2.5 PFLOP/s dense bf16 peak).  `--calibrate-copy` instead times copy_blocks on a known
+number of bytes (the reference copy used to scale hardware byte counters).
 """
 
 from __future__ import annotations
@@ -247,6 +249,53 @@ def measure_swap(dev, steps):
     return res
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix-core peak
+
+
+def prefill_flops(case) -> float:
+    """4 * head_dim flops (two multiply-adds per dim) per (query row, visible key, query head)."""
+    L = case.query_lens.astype(np.int64)
+    n = case.context_lens.astype(np.int64)
+    pairs = int(np.sum(L * (n - L) + L * (L + 1) // 2))
+    return 4.0 * case.spec.head_dim * case.spec.num_heads * pairs
+
+
+def measure_prefill(dev, name, steps, warmup):
+    """pa_prefill on a chunked-prefill workload, both probability precisions, timed with HIP
+    events on the launch stream."""
+    import torch
+    case = W.build_prefill_case(W.PREFILL_CONFIGS[name], device=dev)
+    sp = case.spec
+    q = W.to_torch(case.query, sp.dtype, dev)
+    bt = torch.from_numpy(case.pool.block_tables.astype(np.int32)).to(dev)
+    qsl = torch.from_numpy(case.query_start_loc).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty_like(q)
+    flops = prefill_flops(case)
+    res = {"flops_per_launch": flops, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
+           "num_kv_heads": sp.num_kv_heads, "chunk": str(sp.chunk_lengths),
+           "cached_prefix": str(sp.prefix_lengths)}
+    for mode, bf16_p in (("p16", False), ("p_bf16", True)):
+        def run():
+            ops.prefill(out, q, case.pool.key_cache, case.pool.value_cache, bt, qsl, cl,
+                        float(case.scale), case.max_query_len, bf16_p=bf16_p)
+        for _ in range(max(warmup, 10)):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        tf = flops / (ms * 1e-3) / 1e12
+        res[mode] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                     "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del case
+    return res
+
+
 def run_workload(name, dev, steps, warmup, kernel):
     import torch
     case = W.build_case(W.CONFIGS[name], device=dev)
@@ -350,6 +399,9 @@ def main(argv=None):
         del step
         torch.cuda.empty_cache()
         detail["swap_blocks"] = measure_swap(dev, max(3, args.steps // 4))
+        torch.cuda.empty_cache()
+        for pname in ("prefill_llama7b", "prefill_gqa"):
+            detail[pname] = measure_prefill(dev, pname, args.steps, args.warmup)
         rec["detail"] = detail
     if snaps is not None:
         rec["cpu_baseline"] = cpu_baseline(case, snaps, args.cpu_seconds)
