@@ -7,11 +7,17 @@ Only the test-suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
 from .pa_oracle import (  # noqa: F401
     copy_blocks_ref,
     decode_ref,
+    decode_fp8_ref,
     decode_split_ref,
+    dequantize_fp8,
+    f64_to_fp8_e4m3,
     f64_to_storage,
+    fp8_e4m3_to_f64,
     kv_bytes_per_token,
     prefill_ref,
+    quantize_fp8,
     num_blocks_for,
+    reshape_and_cache_fp8_ref,
     reshape_and_cache_ref,
     resolve_sequence,
     slot_utilization,

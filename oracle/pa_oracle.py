@@ -62,8 +62,10 @@ _BF16_MIN_EXP = -133  # quantum of bfloat16 subnormals: 2**-133
 # element types
 # ---------------------------------------------------------------------------------------
 def storage_to_f64(x, dtype: str) -> np.ndarray:
-    """Exact float64 value of a storage array ("f32": float32, "f16": float16,
+    """Exact float64 value of a storage array ("f64": float64, "f32": float32, "f16": float16,
     "bf16": uint16 raw bits)."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "f16":
@@ -325,3 +327,78 @@ def prefill_ref(query, key_cache, value_cache, block_tables, query_start_loc, co
                 out[q0 + i, h] = _softmax_weighted_sum(K[kv, :last + 1], V[kv, :last + 1],
                                                        q[i, h], sc)
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# 8-bit floating-point KV cache
+# ---------------------------------------------------------------------------------------
+# The cache element type is a serving choice (kv_cache_dtype in the vLLM configuration example
+# of yongjin360.com, §3.2); an 8-bit cache halves the bytes decode streams.  The format is the
+# OCP 8-bit E4M3 ("FN") encoding: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no
+# infinities, S.1111.111 is NaN, largest finite value 448, subnormals m * 2^-9.  A cache keeps
+# one float scale per pool: the stored code is E4M3(x / scale), read back as code * scale.
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of E4M3 codes (uint8 array)."""
+    c = np.asarray(codes).view(np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = np.where((c & 0x80) != 0, -mag, mag)
+    val[(e == 15) & (c & 0x7 == 7)] = np.nan
+    return val
+
+
+def f64_to_fp8_e4m3(x) -> np.ndarray:
+    """Round to E4M3, nearest with ties to even.  Values that round past 448 (|x| > 464) and
+    NaN give the NaN code; the sign of zero is kept.  Callers that saturate clamp first."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.where(np.isfinite(x), np.abs(x), 0.0)
+    _, ex = np.frexp(a)                            # a = f * 2^ex, 0.5 <= f < 1
+    qexp = np.maximum(ex - 4, -9)                  # 3 mantissa bits; subnormal quantum 2^-9
+    r = np.ldexp(np.rint(np.ldexp(a, -qexp)), qexp)
+    _, rex = np.frexp(r)
+    sub = r < 2.0 ** -6
+    e = np.where(sub, 0, rex - 1 + 7)
+    m = np.where(sub, np.ldexp(r, 9), np.ldexp(r, -(rex - 1)) * 8 - 8)
+    code = (e.astype(np.int64) << 3) | m.astype(np.int64)
+    code = np.where(r > FP8_MAX, 0x7F, code)
+    code = np.where(np.isnan(x) | np.isinf(x), 0x7F, code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def quantize_fp8(x, dtype: str, scale) -> np.ndarray:
+    """Codes a cache writer stores for values ``x`` (storage of type ``dtype``): y = x * (1 /
+    scale) in float32 (the reciprocal rounded to float32 once), clamped to +-448 (saturation),
+    then rounded to E4M3."""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = storage_to_f64(x, dtype).astype(np.float32) * inv        # float32 product, nearest
+    y = np.clip(y, np.float32(-FP8_MAX), np.float32(FP8_MAX))
+    return f64_to_fp8_e4m3(y.astype(np.float64))
+
+
+def dequantize_fp8(codes, scale) -> np.ndarray:
+    """float64 values code * scale of an 8-bit cache."""
+    return fp8_e4m3_to_f64(codes) * float(np.float32(scale))
+
+
+def reshape_and_cache_fp8_ref(key, value, key_cache, value_cache, slot_mapping, block_size,
+                              dtype: str, k_scale, v_scale):
+    """reshape_and_cache_ref for an 8-bit cache: token i's K/V (storage of type ``dtype``) are
+    quantized with the pool's scale and stored at slot ``slot_mapping[i]``."""
+    return reshape_and_cache_ref(quantize_fp8(key, dtype, k_scale),
+                                 quantize_fp8(value, dtype, v_scale),
+                                 key_cache, value_cache, slot_mapping, block_size)
+
+
+def decode_fp8_ref(query, key_cache, value_cache, block_tables, context_lens, block_size, scale,
+                   dtype: str, k_scale, v_scale) -> np.ndarray:
+    """Paged decode attention over an 8-bit cache: decode_ref on the dequantized pools (codes
+    times the pool's scale, exactly); ``dtype`` is the query's type."""
+    kc = dequantize_fp8(key_cache, k_scale)
+    vc = dequantize_fp8(value_cache, v_scale)
+    qf = storage_to_f64(query, dtype)
+    return decode_ref(qf, kc, vc, block_tables, context_lens, block_size, scale, "f64")

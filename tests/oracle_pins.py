@@ -530,4 +530,103 @@ def pin_prefill_layout_and_poison(O):
     assert np.array_equal(np.delete(got, np.s_[q0:q1], axis=0), np.delete(base, np.s_[q0:q1], axis=0))
 
 
+# ---------------------------------------------------------------------------------------
+# 8-bit (E4M3) KV cache
+# ---------------------------------------------------------------------------------------
+def _torch_fp8_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_fp8_codes(O):
+    """E4M3 decoding of all 256 codes agrees with torch's float8_e4m3fn, and the format's
+    landmarks come out right: 1.0, the largest finite 448, the smallest normal 2^-6, the
+    smallest subnormal 2^-9, a signed zero, and NaN at S.1111.111."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.fp8_e4m3_to_f64(codes)
+    want = _torch_fp8_values(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6
+    assert got[0x01] == 2.0 ** -9 and got[0xFE] == -448.0 and np.signbit(got[0x80])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.sum(np.isnan(got)) == 2
+
+
+def pin_fp8_rounding(O):
+    """Rounding to E4M3 matches torch's float -> float8_e4m3fn cast (nearest, ties to even)
+    on random values over six decades, on every exact midpoint between neighbouring codes and
+    on signed zeros; past 464 both give NaN."""
+    rng = np.random.default_rng(3)
+    fin = np.unique(_torch_fp8_values(np.arange(256, dtype=np.uint8)))
+    fin = fin[np.isfinite(fin)]
+    mids = (fin[1:] + fin[:-1]) / 2
+    x = np.concatenate([rng.standard_normal(20000) * sc for sc in (1e-3, 0.03, 1.0, 40.0, 300.0)]
+                       + [mids, np.float64([0.0, -0.0, 448.0, 464.0, -464.0, 465.0, 1e9])])
+    x32 = x.astype(np.float32)
+    got = O.f64_to_fp8_e4m3(x32.astype(np.float64))
+    want = torch.from_numpy(x32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+
+
+def pin_fp8_quantize(O):
+    """The cache writer's quantisation saturates at +-448 instead of producing NaN, keeps the
+    relative error within half a unit in the last place (2^-4) over the normal range, and with
+    a power-of-two scale 2^k equals rounding x * 2^-k directly."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(50000) * 3.0).astype(np.float32)
+    bits = x.view(np.uint32) >> np.uint32(16)
+    xb = bits.astype(np.uint16)                      # bfloat16 storage (truncated draw)
+    xv = O.storage_to_f64(xb, "bf16")
+    for sc in (0.01, 0.05, 0.25):
+        codes = O.quantize_fp8(xb, "bf16", sc)
+        back = O.dequantize_fp8(codes, sc)
+        assert not np.any(np.isnan(back))
+        y = xv / sc
+        big = np.abs(y) > 449
+        assert np.all(np.abs(back[big]) == 448.0 * float(np.float32(sc))), "saturation"
+        norm = (np.abs(y) >= 2.0 ** -6) & ~big
+        rel = np.abs(back[norm] - xv[norm]) / np.abs(xv[norm])
+        assert np.max(rel) <= 2.0 ** -4 * (1 + 1e-6), np.max(rel)
+    for k in (-3, 0, 4):
+        got = O.quantize_fp8(xb, "bf16", 2.0 ** k)
+        direct = O.f64_to_fp8_e4m3(np.clip(xv * 2.0 ** -k, -448.0, 448.0))
+        assert np.array_equal(got, direct), k
+
+
+def pin_fp8_cache_and_decode(O):
+    """An 8-bit cache: the writer stores torch's E4M3 cast of the clamped float32 product at
+    each slot (per-element loop), and decode over the scattered 8-bit pools equals torch's
+    float64 SDPA on the contiguous dequantized K/V (codes times each pool's scale), with GQA."""
+    rng = np.random.default_rng(6)
+    NB, H, bs, d, N = 12, 2, 16, 16, 5
+    kc = rng.integers(0, 0x7E, size=(NB, H, bs, d), dtype=np.uint8)
+    vc = rng.integers(0, 0x7E, size=(NB, H, bs, d), dtype=np.uint8)
+    key = W.round_to_storage(rng.standard_normal((N, H, d)).astype(np.float32) * 5, "f16")
+    val = W.round_to_storage(rng.standard_normal((N, H, d)).astype(np.float32) * 5, "f16")
+    slots = np.array([3, 17, 100, -1, 191], np.int64)
+    ks, vs = np.float32(0.02), np.float32(0.125)
+    k2, v2 = O.reshape_and_cache_fp8_ref(key, val, kc, vc, slots, bs, "f16", ks, vs)
+    kl, vl = kc.copy(), vc.copy()
+    for i, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        for src, pool, sc in ((key, kl, ks), (val, vl, vs)):
+            y = np.clip(src[i].astype(np.float32) * (np.float32(1) / sc), -448, 448).astype(np.float32)
+            pool[sl // bs, :, sl % bs, :] = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(k2, kl) and np.array_equal(v2, vl)
+    # decode: 2 sequences over scattered blocks, 4 query heads on 2 KV heads
+    tables = np.array([[7, 2, 9, 0], [5, 11, 1, 4]], np.int32)
+    lens = np.array([50, 33], np.int32)
+    q = W.round_to_storage(rng.standard_normal((2, 4, d)).astype(np.float32), "bf16")
+    out = O.decode_fp8_ref(q, k2, v2, tables, lens, bs, np.float32(0.25), "bf16", ks, vs)
+    for s in range(2):
+        n = int(lens[s])
+        Kc = np.concatenate([k2[b] for b in tables[s]], axis=1)[:, :n]      # [H, n, d] codes
+        Vc = np.concatenate([v2[b] for b in tables[s]], axis=1)[:, :n]
+        K = _torch_fp8_values(Kc) * float(ks)
+        V = _torch_fp8_values(Vc) * float(vs)
+        ref = _sdpa(O.storage_to_f64(q[s], "bf16"), K, V, np.float32(0.25))
+        assert np.max(np.abs(out[s] - ref)) <= 1e-12, s
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

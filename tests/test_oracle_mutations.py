@@ -37,7 +37,7 @@ MUTATIONS = [
     ("value not written", "        vc[b, :, o, :] = value[i]\n", "        vc[b, :, o, :] = key[i]\n"),
     ("copy direction", "kc[dst] = k0[src]", "kc[src] = k0[dst]"),
     ("V block not copied", "        vc[dst] = v0[src]\n", "        pass\n"),
-    ("bf16 truncation", "r = np.ldexp(np.rint(", "r = np.ldexp(np.trunc("),
+    ("bf16 truncation", "r = np.ldexp(np.rint(np.ldexp(xf,", "r = np.ldexp(np.trunc(np.ldexp(xf,"),
     ("bf16 precision", "qexp = np.maximum(e - 8,", "qexp = np.maximum(e - 9,"),
     ("bf16 decode shift", "<< np.uint32(16)\n        return bits", "<< np.uint32(15)\n        return bits"),
     ("merge weight", "w = np.array([l * math.exp(m - M) for m, l, _ in parts])",
@@ -59,6 +59,15 @@ MUTATIONS = [
      "                kv = h % Hkv\n                out[q0 + i, h]"),
     ("prefill row offset", "q = storage_to_f64(query[q0:q1], dtype)", "q = storage_to_f64(query[0:L], dtype)"),
     ("prefill no length guard", "if L <= 0 or n < L:", "if L <= 0:"),
+    ("fp8 exponent bias", "np.exp2((e - 7).astype(np.float64))", "np.exp2((e - 8).astype(np.float64))"),
+    ("fp8 subnormal quantum", "mag = np.where(e == 0, m * 2.0 ** -9,", "mag = np.where(e == 0, m * 2.0 ** -10,"),
+    ("fp8 sign dropped", "    val = np.where((c & 0x80) != 0, -mag, mag)\n", "    val = mag\n"),
+    ("fp8 rounding truncates", "r = np.ldexp(np.rint(np.ldexp(a, -qexp)), qexp)\n    _, rex",
+     "r = np.ldexp(np.floor(np.ldexp(a, -qexp)), qexp)\n    _, rex"),
+    ("fp8 mantissa width", "qexp = np.maximum(ex - 4, -9)", "qexp = np.maximum(ex - 3, -9)"),
+    ("fp8 no saturation", "    y = np.clip(y, np.float32(-FP8_MAX), np.float32(FP8_MAX))\n", ""),
+    ("fp8 scale multiplies", "inv = np.float32(1.0) / np.float32(scale)", "inv = np.float32(scale)"),
+    ("fp8 value scale for keys", "    kc = dequantize_fp8(key_cache, k_scale)", "    kc = dequantize_fp8(key_cache, v_scale)"),
 ]
 
 
