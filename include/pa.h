@@ -49,7 +49,10 @@ typedef enum {
   PA_ERR_LAUNCH = 5        /* the HIP runtime reported an error when launching */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element types.  PA_FP8_E4M3 (OCP 8-bit E4M3, "FN" encoding: bias 7, largest finite 448, no
+ * infinities, S.1111.111 = NaN) is a cache element type only: pools of the _fp8 entry points,
+ * pa_copy_blocks and pa_swap_blocks. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Kernel family for pa_decode_ex.  PA_KERNEL_AUTO is what pa_decode uses. */
 typedef enum {
@@ -203,7 +206,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
  *
  *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim]  (updated in place)
  *   block_mapping  int64 [num_pairs][2]
- * Supported: num_kv_heads * block_size * head_dim * sizeof(dtype) a multiple of 16 bytes.
+ * Supported: num_kv_heads * block_size * head_dim * sizeof(dtype) a multiple of 16 bytes; dtype
+ * may be PA_FP8_E4M3 (1 byte).
  */
 pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
@@ -227,7 +231,8 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bloc
  * (hipHostMalloc, or a torch tensor created with pin_memory=True), which the kernel reads or
  * writes over the host link.  The pools are not synchronised with the host: the caller waits
  * on `stream` before reading a host pool.
- * Supported: num_kv_heads * block_size * head_dim * sizeof(dtype) a multiple of 16 bytes.
+ * Supported: num_kv_heads * block_size * head_dim * sizeof(dtype) a multiple of 16 bytes; dtype
+ * may be PA_FP8_E4M3 (1 byte).
  */
 pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
                          int32_t src_num_blocks, void* dst_key_cache, void* dst_value_cache,
@@ -269,6 +274,50 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache, const 
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
                      float scale, pa_dtype dtype, uint32_t flags, void* stream);
+
+/*
+ * 8-bit KV cache.  The cache element type is a serving choice (kv_cache_dtype in the vLLM
+ * configuration on the yongjin360.com page, §3.2); an E4M3 cache halves the bytes decode
+ * streams.  Each pool has one positive float scale: a stored code c stands for c * scale.
+ *
+ * pa_reshape_and_cache_fp8 — pa_reshape_and_cache into E4M3 pools: for token i with a slot in
+ * the pool, every element x of key[i] is stored as E4M3(clamp(x * (1/k_scale), -448, 448)),
+ * with 1/k_scale rounded to float once, the product in float, and nearest-even rounding to
+ * E4M3 (value alike with v_scale).  Negative or out-of-pool slots are skipped.
+ *   key, value  [num_tokens][num_kv_heads][head_dim]  dtype (PA_F16 or PA_BF16)
+ *   key_cache, value_cache  uint8 [num_blocks][num_kv_heads][block_size][head_dim]
+ * Supported: head_dim a multiple of 8, at most 1024.  Scales must be finite and > 0.
+ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                   void* value_cache, const int64_t* slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                                   float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode_fp8 — pa_decode over E4M3 pools: the result is decode attention over
+ * K = code * k_scale and V = code * v_scale (exact values), with fp32 accumulation.  query and
+ * out are dtype (PA_F16 or PA_BF16); pools are uint8 as above; partition_size, workspace
+ * (pa_decode_workspace_bytes with the same sizes), flags and errors as pa_decode_ex.
+ * pa_decode_fp8_partitions is its first launch (pa_decode_merge, with the same dtype, is the
+ * second).  Supported: head_dim 128, block_size 16 or 32.
+ */
+pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                        pa_dtype dtype, float k_scale, float v_scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, float scale, pa_dtype dtype,
+                                   float k_scale, float v_scale, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

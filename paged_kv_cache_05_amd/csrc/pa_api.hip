@@ -16,15 +16,25 @@ constexpr long kMinPartition = 256;      // tokens per split-KV partition, lower
 constexpr long kMaxPartition = 2048;     // and upper bound
 constexpr long kTargetWorkgroups = 2048; // 256 CUs x 8 resident 4-wave workgroups
 
+// Element types of query / output / 16-bit-or-wider caches.
 bool dtype_of(pa_dtype d, DT* out) {
   switch (d) {
     case PA_F32: *out = DT::F32; return true;
     case PA_F16: *out = DT::F16; return true;
     case PA_BF16: *out = DT::BF16; return true;
+    default: break;
   }
   return false;
 }
-int elem_bytes(DT d) { return d == DT::F32 ? 4 : 2; }
+// Element types a pool may hold (the block copies move bytes of any of them).
+bool pool_dtype_of(pa_dtype d, DT* out) {
+  if (d == PA_FP8_E4M3) {
+    *out = DT::FP8;
+    return true;
+  }
+  return dtype_of(d, out);
+}
+int elem_bytes(DT d) { return d == DT::F32 ? 4 : d == DT::FP8 ? 1 : 2; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Plan {
@@ -183,6 +193,7 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   p.partition = pl.partition;
   p.max_parts = pl.max_parts;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.v_scale = 1.0f;
 
   const long grid = (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts;
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
@@ -277,7 +288,7 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bloc
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
   DT dt;
-  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  if (!pool_dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
     return PA_ERR_BAD_SHAPE;
   const long block_bytes = (long)num_kv_heads * block_size * head_dim * elem_bytes(dt);
@@ -297,7 +308,7 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          pa_dtype dtype, void* stream) {
   DT dt;
-  if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  if (!pool_dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       src_num_blocks < 0 || dst_num_blocks < 0)
     return PA_ERR_BAD_SHAPE;
@@ -363,6 +374,102 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache, const 
   (void)hipGetLastError();
   return launch_status(pa::launch_prefill_mfma(dt, block_size, split_p, p, (int)grid,
                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                   void* value_cache, const int64_t* slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                                   float k_scale, float v_scale, void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt) || dt == DT::F32) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (head_dim % 8 != 0 || head_dim > 1024) return PA_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return PA_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_reshape_and_cache_fp8(
+      dt, key, value, key_cache, value_cache, slot_mapping, num_tokens, head_dim, block_size,
+      num_blocks, num_kv_heads, 1.0f / k_scale, 1.0f / v_scale,
+      reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, float scale, pa_dtype dtype,
+                                   float k_scale, float v_scale, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   void* stream) {
+  DT dt;
+  if (!dtype_of(dtype, &dt) || dt == DT::F32) return PA_ERR_UNSUPPORTED;
+  pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, partition_size);
+  if (st != PA_OK) return st;
+  if (head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_PTR;
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return PA_ERR_BAD_SHAPE;
+  const Plan pl = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, partition_size);
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return PA_ERR_WORKSPACE;
+  const int G = num_heads / num_kv_heads;
+  const int gt = std::min(heads_per_wg(false, G), 2);   // 16 fp32 outputs per lane per head
+
+  pa::DecodeParams p;
+  p.out = out;
+  p.q = query;
+  p.kc = key_cache;
+  p.vc = value_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.ws_ml = pl.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
+  p.ws_o = pl.ws_bytes ? reinterpret_cast<float*>((char*)workspace + pl.ws_ml_bytes) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = G;
+  p.head_chunks = G / gt;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.partition = pl.partition;
+  p.max_parts = pl.max_parts;
+  p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  p.v_scale = v_scale;
+  const long grid = (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts;
+  if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
+  (void)hipGetLastError();
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
+  return launch_status(pa::launch_decode_valu_fp8(dt, head_dim, block_size, gt, stream_kv, p,
+                                                  (int)grid,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                        pa_dtype dtype, float k_scale, float v_scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  pa_status st = pa_decode_fp8_partitions(out, query, key_cache, value_cache, block_tables,
+                                          context_lens, num_seqs, num_heads, num_kv_heads,
+                                          head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                          scale, dtype, k_scale, v_scale, partition_size,
+                                          workspace, workspace_bytes, flags, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_merge(out, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                         block_size, max_blocks_per_seq, dtype, partition_size, workspace,
+                         workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -10,6 +10,8 @@
 // summary of Kwon et al. (xasun.com) §一 and §二, sharing item).
 // swap_blocks: a preempted sequence's blocks move to a CPU block pool and back (same page,
 // §二: block pools on both GPU and CPU; recovery by swapping).
+// reshape_and_cache into an 8-bit cache quantizes instead of copying: the cache element type
+// is a serving choice (kv_cache_dtype in the vLLM configuration of yongjin360.com, §3.2).
 #include "pa_common.h"
 
 namespace pa {
@@ -33,6 +35,36 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const size_t dst = ((size_t)(b * num_kv_heads + h) * block_size + off) * row_vecs + j;
     kc[dst] = ks[v];
     vc[dst] = vs[v];
+  }
+}
+
+// reshape_and_cache into an 8-bit E4M3 cache: each 16-byte vector of a 16-bit source row (8
+// elements) becomes 8 bytes of the cache row: x * (1 / scale) in fp32, clamped to +-448,
+// rounded to nearest-even.
+template <DT dt>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint2* __restrict__ kc,
+    uint2* __restrict__ vc, const int64_t* __restrict__ slots, int row_vecs, int block_size,
+    int64_t num_slots, int num_kv_heads, float k_inv, float v_inv) {
+  static_assert(Elem<dt>::kPerVec == 8, "16-bit source elements");
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;   // padding, or out of the pool
+  const int64_t b = slot / block_size;
+  const int off = (int)(slot - b * block_size);
+  const int total = num_kv_heads * row_vecs;
+  const uint4* ks = key + (size_t)i * total;
+  const uint4* vs = value + (size_t)i * total;
+  for (int v = threadIdx.x; v < total; v += blockDim.x) {
+    const int h = v / row_vecs, j = v - h * row_vecs;
+    const size_t dst = ((size_t)(b * num_kv_heads + h) * block_size + off) * row_vecs + j;
+    float f[8];
+    Elem<dt>::unpack(ks[v], f);
+    kc[dst] = make_uint2(fp8_pack4(f[0] * k_inv, f[1] * k_inv, f[2] * k_inv, f[3] * k_inv),
+                         fp8_pack4(f[4] * k_inv, f[5] * k_inv, f[6] * k_inv, f[7] * k_inv));
+    Elem<dt>::unpack(vs[v], f);
+    vc[dst] = make_uint2(fp8_pack4(f[0] * v_inv, f[1] * v_inv, f[2] * v_inv, f[3] * v_inv),
+                         fp8_pack4(f[4] * v_inv, f[5] * v_inv, f[6] * v_inv, f[7] * v_inv));
   }
 }
 
@@ -80,6 +112,27 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(num_tokens), dim3(256), 0, st,
                      (const uint4*)key, (const uint4*)value, (uint4*)kc, (uint4*)vc, slots,
                      row_vecs, block_size, (int64_t)num_blocks * block_size, num_kv_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(DT dt, const void* key, const void* value, void* kc,
+                                        void* vc, const int64_t* slots, int num_tokens,
+                                        int head_dim, int block_size, int num_blocks,
+                                        int num_kv_heads, float k_inv, float v_inv,
+                                        hipStream_t st) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int row_vecs = head_dim / 8;   // 16-byte source vectors per head row
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  if (dt == DT::BF16)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT::BF16>, dim3(num_tokens), dim3(256), 0, st,
+                       (const uint4*)key, (const uint4*)value, (uint2*)kc, (uint2*)vc, slots,
+                       row_vecs, block_size, num_slots, num_kv_heads, k_inv, v_inv);
+  else if (dt == DT::F16)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<DT::F16>, dim3(num_tokens), dim3(256), 0, st,
+                       (const uint4*)key, (const uint4*)value, (uint2*)kc, (uint2*)vc, slots,
+                       row_vecs, block_size, num_slots, num_kv_heads, k_inv, v_inv);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ constexpr int kWave = 64;
 // Element types.  Every kernel moves data in 16-byte vectors (one global_load_dwordx4 per
 // lane) and computes in fp32.
 // ---------------------------------------------------------------------------------------
-enum class DT { F32, F16, BF16 };
+enum class DT { F32, F16, BF16, FP8 };   // FP8: OCP E4M3 ("FN"), cache element only
 
 template <DT> struct Elem;
 
@@ -87,6 +87,39 @@ template <> struct Elem<DT::BF16> {
     return make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
+
+// 8-bit E4M3 cache elements (OCP "FN" encoding: bias 7, max 448, no infinities).  gfx950's
+// v_cvt_pk_f32_fp8 / v_cvt_pk_fp8_f32 use this encoding; the conversion to 8 bits rounds to
+// nearest-even and turns values past 464 into NaN, so writers clamp to +-448 first.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <> struct Elem<DT::FP8> {
+  static constexpr int kBytes = 1;
+  static constexpr int kPerVec = 16;
+  __device__ __forceinline__ static void unpack(const uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  }
+};
+
+// Saturate to the largest finite E4M3 magnitude; NaN passes through (and encodes as NaN).
+__device__ __forceinline__ float fp8_saturate(float y) {
+  return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+}
+// four floats -> four E4M3 codes in one word (byte i = element i)
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_saturate(a), fp8_saturate(b), w, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_saturate(c), fp8_saturate(d), w, true);
+  return w;
+}
 
 // ---------------------------------------------------------------------------------------
 // Cross-lane reductions inside groups of N consecutive lanes (N = 1, 8, 16, 32).  Every step
@@ -177,7 +210,8 @@ struct DecodeParams {
   int32_t max_blocks_per_seq, num_blocks;
   int32_t partition;         // tokens per partition (multiple of 16)
   int32_t max_parts;         // partitions a full table can hold
-  float scale_log2;          // scale * log2(e)
+  float scale_log2;          // scale * log2(e) (times the key scale of an 8-bit cache)
+  float v_scale;             // value scale of an 8-bit cache (1 otherwise)
 };
 
 struct MergeParams {
@@ -206,6 +240,13 @@ struct PrefillParams {
 // host-side launchers (return hipSuccess or the launch error)
 hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
                               bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_valu_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
+                                  bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_reshape_and_cache_fp8(DT dt, const void* key, const void* value, void* kc,
+                                        void* vc, const int64_t* slots, int num_tokens,
+                                        int head_dim, int block_size, int num_blocks,
+                                        int num_kv_heads, float k_inv, float v_inv,
+                                        hipStream_t st);
 hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
                               bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const PrefillParams& p,

@@ -23,10 +23,12 @@
 namespace pa {
 namespace {
 
-template <DT dt, int D, int BS, int GT>
+template <DT dt, DT kt, int D, int BS, int GT>
 struct ValuCfg {
-  using E = Elem<dt>;
+  using E = Elem<kt>;                        // cache elements
+  using Q = Elem<dt>;                        // query / output elements
   static constexpr int EPL = E::kPerVec;     // elements per lane per 16-byte vector
+  static constexpr int QV = EPL / Q::kPerVec;  // query vectors per lane (2 for an 8-bit cache)
   static constexpr int LPT = D / EPL;        // lanes per token row
   static constexpr int TPI = kWave / LPT;    // tokens per wave load instruction
   static constexpr int NI = 16 / TPI;        // load instructions per 16-token chunk
@@ -36,11 +38,12 @@ struct ValuCfg {
   static_assert(BS % 16 == 0, "block size must be a multiple of 16");
 };
 
-template <DT dt, int D, int BS, int GT, bool STREAM>
+template <DT dt, DT kt, int D, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) {
-  using C = ValuCfg<dt, D, BS, GT>;
+  using C = ValuCfg<dt, kt, D, BS, GT>;
   using E = typename C::E;
-  constexpr int EPL = C::EPL, LPT = C::LPT, TPI = C::TPI, NI = C::NI, CPB = C::CPB;
+  using Q = typename C::Q;
+  constexpr int EPL = C::EPL, LPT = C::LPT, TPI = C::TPI, NI = C::NI, CPB = C::CPB, QV = C::QV;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
@@ -64,11 +67,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int ch_begin = part * (p.partition / 16);
-  uint4 qraw[GT];
+  uint4 qraw[GT][QV];
 #pragma unroll
   for (int h = 0; h < GT; ++h)
-    qraw[h] = *reinterpret_cast<const uint4*>((const char*)p.q +
-                                              (q_row0 + (size_t)h * D + col * EPL) * E::kBytes);
+#pragma unroll
+    for (int v = 0; v < QV; ++v)
+      qraw[h][v] = *reinterpret_cast<const uint4*>(
+          (const char*)p.q + (q_row0 + (size_t)h * D + col * EPL) * Q::kBytes + 16 * v);
   int ent_first = -1;
   {
     const int my_ch = ch_begin + wave + 4 * lane;
@@ -85,17 +90,20 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       const float z[EPL] = {};
 #pragma unroll
       for (int h = 0; h < GT; ++h)
-        *reinterpret_cast<uint4*>((char*)p.out + (q_row0 + (size_t)h * D + col * EPL) * E::kBytes) =
-            E::pack(z);
+#pragma unroll
+        for (int v = 0; v < QV; ++v)
+          *reinterpret_cast<uint4*>((char*)p.out + (q_row0 + (size_t)h * D + col * EPL) * Q::kBytes +
+                                    16 * v) = Q::pack(z);
     }
     return;
   }
 
-  // query, pre-scaled by scale*log2(e), as fp32
+  // query, pre-scaled by scale*log2(e) (and the key scale of an 8-bit cache), as fp32
   float qf[GT][EPL];
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
-    E::unpack(qraw[h], qf[h]);
+#pragma unroll
+    for (int v = 0; v < QV; ++v) Q::unpack(qraw[h][v], qf[h] + v * Q::kPerVec);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[h][e] *= p.scale_log2;
   }
@@ -268,12 +276,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
 #pragma unroll
       for (int e = 0; e < EPL; ++e) O[e] = fmaf(wt, s_o[w][h][cc * EPL + e], O[e]);
     }
-    const float inv = 1.0f / L;
+    const float inv = p.v_scale / L;   // an 8-bit cache's value scale factors out of the sum
 #pragma unroll
     for (int e = 0; e < EPL; ++e) O[e] *= inv;
     const size_t qrow = q_row0 + (size_t)h * D;
     if (nparts == 1) {
-      *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * EPL) * E::kBytes) = E::pack(O);
+#pragma unroll
+      for (int v = 0; v < QV; ++v)
+        *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * EPL) * Q::kBytes + 16 * v) =
+            Q::pack(O + v * Q::kPerVec);
     } else {
       const size_t slot = (size_t)(s * p.num_heads + h0 + h) * p.max_parts + part;
       float* po = p.ws_o + slot * D + cc * EPL;
@@ -285,30 +296,47 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
 }
 
-template <DT dt, int D, int BS, bool ST>
+template <DT dt, DT kt, int D, int BS, bool ST>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
   switch (gt) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 1, ST>), dim3(grid), dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 2, ST>), dim3(grid), dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<dt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 1, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 2, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4:
+    case 8:
+      // an 8-bit cache row gives each lane 16 elements: more than 2 heads per workgroup would
+      // hold 64+ fp32 outputs per lane and drop occupancy to one wave per SIMD
+      if constexpr (kt != DT::FP8) {
+        if (gt == 4)
+          hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p);
+        else
+          hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <DT dt, int D, int BS>
+template <DT dt, DT kt, int D, int BS>
 hipError_t launch_st(bool stream_kv, int gt, const DecodeParams& p, int grid, hipStream_t st) {
-  return stream_kv ? launch_gt<dt, D, BS, true>(gt, p, grid, st)
-                   : launch_gt<dt, D, BS, false>(gt, p, grid, st);
+  return stream_kv ? launch_gt<dt, kt, D, BS, true>(gt, p, grid, st)
+                   : launch_gt<dt, kt, D, BS, false>(gt, p, grid, st);
 }
 
 template <DT dt>
 hipError_t launch_dt(int d, int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
-  if (d == 64 && bs == 16) return launch_st<dt, 64, 16>(sk, gt, p, grid, st);
-  if (d == 64 && bs == 32) return launch_st<dt, 64, 32>(sk, gt, p, grid, st);
-  if (d == 128 && bs == 16) return launch_st<dt, 128, 16>(sk, gt, p, grid, st);
-  if (d == 128 && bs == 32) return launch_st<dt, 128, 32>(sk, gt, p, grid, st);
+  if (d == 64 && bs == 16) return launch_st<dt, dt, 64, 16>(sk, gt, p, grid, st);
+  if (d == 64 && bs == 32) return launch_st<dt, dt, 64, 32>(sk, gt, p, grid, st);
+  if (d == 128 && bs == 16) return launch_st<dt, dt, 128, 16>(sk, gt, p, grid, st);
+  if (d == 128 && bs == 32) return launch_st<dt, dt, 128, 32>(sk, gt, p, grid, st);
+  return hipErrorInvalidValue;
+}
+
+template <DT dt>
+hipError_t launch_fp8(int d, int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
+  if (d == 128 && bs == 16) return launch_st<dt, DT::FP8, 128, 16>(sk, gt, p, grid, st);
+  if (d == 128 && bs == 32) return launch_st<dt, DT::FP8, 128, 32>(sk, gt, p, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -320,6 +348,17 @@ hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per
     case DT::F32: return launch_dt<DT::F32>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
     case DT::F16: return launch_dt<DT::F16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
     case DT::BF16: return launch_dt<DT::BF16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_valu_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
+                                  bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
+  switch (dt) {
+    case DT::F16: return launch_fp8<DT::F16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
+    case DT::BF16: return launch_fp8<DT::BF16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
+    default: break;
   }
   return hipErrorInvalidValue;
 }

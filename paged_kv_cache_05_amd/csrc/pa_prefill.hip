@@ -248,23 +248,30 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
     if (more) issue(k + 1, ent_next);
 
     // The tile is consumed in two 32-token halves, each a complete online-softmax step
-    // (scores, max, rescale, probabilities, products), which keeps half as many scores live.
+    // (scores, max, rescale, probabilities, products).  Both halves' scores are issued first,
+    // so the matrix cores work on the second half's scores while the vector ALUs run the
+    // first half's softmax.
+    f32x4 sts[2][2][2];   // [half][16-token block][row block]
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (!(wave_active && k * kTile + 32 * h < w_kv_end)) continue;   // wave-uniform
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int j = 2 * h + jb;
+        sts[h][jb][0] = sts[h][jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 a = s_k[buf][(16 * j + lr) * 16 + ((4 * c + lg) ^ lr)];
+          sts[h][jb][0] = M::mma(a, qb[0][c], sts[h][jb][0]);
+          sts[h][jb][1] = M::mma(a, qb[1][c], sts[h][jb][1]);
+        }
+      }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tstart = k * kTile + 32 * h;
       if (!(wave_active && tstart < w_kv_end)) continue;   // wave-uniform
-      f32x4 st[2][2];   // [16-token block][row block]
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int j = 2 * h + jb;
-        st[jb][0] = st[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 a = s_k[buf][(16 * j + lr) * 16 + ((4 * c + lg) ^ lr)];
-          st[jb][0] = M::mma(a, qb[0][c], st[jb][0]);
-          st[jb][1] = M::mma(a, qb[1][c], st[jb][1]);
-        }
-      }
+      f32x4 (&st)[2][2] = sts[h];
       // Causal mask (only where the half reaches past some row's last position) and the row
       // max, both on the raw scores: scale > 0, so the max commutes with it.  The masking
       // branch holds a scheduling barrier so that it stays a branch (halves every row sees

@@ -46,6 +46,12 @@ _SIGNATURES = {
     "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
     "pa_swap_blocks": (_c_int, [_p, _p, _c_int, _p, _p, _c_int, _p] + [_c_int] * 5 + [_p]),
     "pa_prefill": (_c_int, [_p] * 7 + [_c_int] * 8 + [_c_float, _c_int, ctypes.c_uint32, _p]),
+    "pa_reshape_and_cache_fp8": (_c_int, [_p] * 5 + [_c_int] * 6 + [_c_float, _c_float, _p]),
+    "pa_decode_fp8": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_float, _c_float,
+                                                      _c_int, _p, _c_size, ctypes.c_uint32, _p]),
+    "pa_decode_fp8_partitions": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_float,
+                                                                 _c_float, _c_int, _p, _c_size,
+                                                                 ctypes.c_uint32, _p]),
 }
 
 
@@ -85,7 +91,8 @@ def _check(status: int, what: str) -> None:
 # ---------------------------------------------------------------------------------------
 def _dtype_code(t) -> int:
     import torch
-    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.uint8: 3,
+             torch.float8_e4m3fn: 3}
     if t.dtype not in codes:
         raise TypeError(f"unsupported element type {t.dtype}")
     return codes[t.dtype]
@@ -290,3 +297,83 @@ def prefill(out, query, key_cache, value_cache, block_tables, query_start_loc, c
                              float(scale), _dtype_code(query),
                              PA_PREFILL_BF16_P if bf16_p else 0, _stream(dev, stream)), "pa_prefill")
     return out
+
+
+PA_FP8_E4M3 = 3
+
+
+def _fp8_pools(key_cache, value_cache):
+    import torch
+    for t in (key_cache, value_cache):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("8-bit pools must be uint8 or float8_e4m3fn tensors")
+    if tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("key_cache and value_cache must match")
+    return key_cache.shape
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, *,
+                          stream=None):
+    """pa_reshape_and_cache_fp8: quantize key/value [N, Hkv, d] (f16/bf16) into E4M3 pools."""
+    import torch
+    dev = _dev(key, value, key_cache, value_cache, slot_mapping)
+    NB, Hkv, BS, D = _fp8_pools(key_cache, value_cache)
+    N = key.shape[0]
+    if tuple(key.shape) != (N, Hkv, D) or tuple(value.shape) != (N, Hkv, D) or key.dtype != value.dtype:
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] of one type")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (N,):
+        raise TypeError("slot_mapping must be int64 [num_tokens]")
+    _check(load().pa_reshape_and_cache_fp8(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                           _ptr(slot_mapping), N, Hkv, D, BS, NB, _dtype_code(key),
+                                           float(k_scale), float(v_scale), _stream(dev, stream)),
+           "pa_reshape_and_cache_fp8")
+
+
+def _decode_fp8_args(out, query, key_cache, value_cache, block_tables, context_lens):
+    import torch
+    S, Hq, D = query.shape
+    NB, Hkv, BS, D2 = _fp8_pools(key_cache, value_cache)
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or out.dtype != query.dtype:
+        raise ValueError("out must match the query; pools [num_blocks, num_kv_heads, block_size, head_dim]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and context_lens [num_seqs]")
+    return S, Hq, Hkv, D, BS, NB, block_tables.shape[1]
+
+
+def decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens, scale, k_scale,
+               v_scale, *, partition_size=0, shared_blocks=False, workspace=None, stream=None):
+    """pa_decode_fp8: paged decode attention over E4M3 pools (codes times k_scale / v_scale)."""
+    import torch
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    S, Hq, Hkv, D, BS, NB, maxb = _decode_fp8_args(out, query, key_cache, value_cache,
+                                                   block_tables, context_lens)
+    need = workspace_bytes(S, Hq, Hkv, D, BS, maxb, partition_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_fp8(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS, NB, maxb,
+                                float(scale), _dtype_code(query), float(k_scale), float(v_scale),
+                                int(partition_size), _ptr(workspace), wsb,
+                                PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+                                _stream(dev, stream)), "pa_decode_fp8")
+    return out
+
+
+def decode_fp8_partitions(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                          k_scale, v_scale, workspace, *, partition_size=0, shared_blocks=False,
+                          stream=None):
+    """pa_decode_fp8_partitions: the first of pa_decode_fp8's two launches."""
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    S, Hq, Hkv, D, BS, NB, maxb = _decode_fp8_args(out, query, key_cache, value_cache,
+                                                   block_tables, context_lens)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_fp8_partitions(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                           _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D,
+                                           BS, NB, maxb, float(scale), _dtype_code(query),
+                                           float(k_scale), float(v_scale), int(partition_size),
+                                           _ptr(workspace), wsb,
+                                           PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
+                                           _stream(dev, stream)), "pa_decode_fp8_partitions")

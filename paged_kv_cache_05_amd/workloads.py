@@ -31,8 +31,11 @@ import numpy as np
 from .block_manager import BlockManager
 
 DTYPES = ("f32", "f16", "bf16")
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}
+# 8-bit caches hold E4M3 codes of N(0,1) draws divided by this scale (and clipped to +-6.5
+# sigma so no draw leaves the format's +-448 range): 6.5 * 64 = 416.
+FP8_DRAW_SCALE = 1.0 / 64.0
 
 
 # ---------------------------------------------------------------------------------------
@@ -57,10 +60,16 @@ def round_to_storage(x32, dtype: str) -> np.ndarray:
         return x32.astype(np.float16)
     if dtype == "bf16":
         return float32_to_bf16_bits(x32)
+    if dtype == "fp8":   # random E4M3 codes: torch's cast of the clipped, scaled draw
+        import torch
+        y = np.clip(x32, -6.5, 6.5) / np.float32(FP8_DRAW_SCALE)
+        return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def nan_storage(dtype: str):
+    if dtype == "fp8":
+        return np.uint8(NAN_BITS["fp8"])
     if dtype == "f32":
         return np.float32(np.nan)
     if dtype == "f16":
@@ -69,7 +78,7 @@ def nan_storage(dtype: str):
 
 
 def storage_np_dtype(dtype: str):
-    return {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    return {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}[dtype]
 
 
 # ---------------------------------------------------------------------------------------
@@ -95,6 +104,7 @@ class CaseSpec:
     fork: bool = False                 # parallel-sampling sibling per sequence before the step
     q_scale: float = 1.0               # multiplies q (peaky-softmax stress when large)
     max_blocks_per_seq: int | None = None  # table width; None: the widest sequence
+    kv_dtype: str | None = None        # pool element type when it differs ("fp8")
 
 
 def scaled(spec: CaseSpec, **kw) -> CaseSpec:
@@ -114,6 +124,9 @@ CONFIGS = {
                          partition_size=512),
     "shared_prefix": CaseSpec("shared_prefix", 5, 64, 32, 32, 128, "f16", 16,
                               ("uniform", 1, 512), shared_prefix=1024, fork=True),
+    # the Llama-7B-shaped decode step over an 8-bit E4M3 cache (bf16 queries and new tokens)
+    "llama7b_bs16_fp8": CaseSpec("llama7b_bs16_fp8", 3, 256, 32, 32, 128, "bf16", 16,
+                                 ("lognormal", 700.0, 1.0, 16, 4096), kv_dtype="fp8"),
 }
 
 
@@ -308,16 +321,17 @@ def build_case(spec: CaseSpec, *, device=None, poison=False, table_fill=-1,
         case.sibling_lens = lay["sib_lens"]
 
     shape = (NB, Hkv, bs, d)
+    pdt = spec.kv_dtype or dt          # pool element type
     if device is None:
-        kc = round_to_storage(np.random.default_rng(c_k).standard_normal(shape, dtype=np.float32), dt)
-        vc = round_to_storage(np.random.default_rng(c_v).standard_normal(shape, dtype=np.float32), dt)
+        kc = round_to_storage(np.random.default_rng(c_k).standard_normal(shape, dtype=np.float32), pdt)
+        vc = round_to_storage(np.random.default_rng(c_v).standard_normal(shape, dtype=np.float32), pdt)
         if poison:
             dead = ~live
             if not free_mode and len(slots):
                 # the step's own slots are written by reshape_and_cache before decode reads them
                 dead[slots] = True
             for pool in (kc, vc):
-                _slot_view(pool)[:, dead, :] = nan_storage(dt)
+                _slot_view(pool)[:, dead, :] = nan_storage(pdt)
         case.key_cache, case.value_cache = kc, vc
         if keep_contiguous and not spec.shared_prefix:
             case.contiguous = []
@@ -327,12 +341,14 @@ def build_case(spec: CaseSpec, *, device=None, poison=False, table_fill=-1,
                 K = kv_view[:, ts, :].copy()
                 V = vv_view[:, ts, :].copy()
                 if not free_mode:
+                    if pdt != dt:
+                        raise ValueError("contiguous K/V of a quantized cache need free-slot mode")
                     K[:, -1, :] = case.new_key[s]
                     V[:, -1, :] = case.new_value[s]
                 case.contiguous.append((K, V))
     else:
-        case.key_cache = _device_pool(shape, dt, c_k, device)
-        case.value_cache = _device_pool(shape, dt, c_v, device)
+        case.key_cache = _device_pool(shape, pdt, c_k, device)
+        case.value_cache = _device_pool(shape, pdt, c_v, device)
         if poison:
             raise ValueError("poisoned pools are host-generated only")
     return case
@@ -343,7 +359,8 @@ def build_case(spec: CaseSpec, *, device=None, poison=False, table_fill=-1,
 # ---------------------------------------------------------------------------------------
 def torch_dtype(dtype: str):
     import torch
-    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "fp8": torch.uint8}[dtype]
 
 
 def to_torch(arr, dtype: str, device):
@@ -356,6 +373,8 @@ def to_torch(arr, dtype: str, device):
         t = torch.from_numpy(a.view(np.float16))
     elif dtype == "f32":
         t = torch.from_numpy(a.view(np.float32))
+    elif dtype == "fp8":
+        t = torch.from_numpy(a.view(np.uint8))
     else:
         t = torch.from_numpy(a)
     return t.to(device)
@@ -371,6 +390,8 @@ def from_torch(t, dtype: str) -> np.ndarray:
         return t.numpy().view(np.float16)
     if dtype == "f32":
         return t.numpy().view(np.float32)
+    if dtype == "fp8":
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
@@ -382,8 +403,12 @@ def _device_pool(shape, dtype, seed_seq, device):
     step = max(1, (1 << 26) // max(1, int(np.prod(shape[1:]))))
     for b0 in range(0, shape[0], step):
         b1 = min(shape[0], b0 + step)
-        out[b0:b1] = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device,
-                                 dtype=torch.float32).to(out.dtype)
+        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device,
+                        dtype=torch.float32)
+        if dtype == "fp8":
+            out[b0:b1] = (x.clamp(-6.5, 6.5) / FP8_DRAW_SCALE).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            out[b0:b1] = x.to(out.dtype)
     return out
 
 

@@ -140,3 +140,31 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, flags=0x1, out=0) == 1      # the bf16-probabilities flag is accepted
     assert _prefill(lib, S=0, out=0) == 0            # nothing to do
     assert _prefill(lib, maxq=0, out=0) == 0
+
+
+def test_fp8_argument_errors(lib):
+    p = ctypes.c_void_p(1)
+    f = lib.pa_reshape_and_cache_fp8
+    assert f(p, p, p, p, None, 4, 2, 128, 16, 64, 2, 0.1, 0.1, None) == 1
+    assert f(p, p, p, p, p, 4, 2, 128, 16, 64, 0, 0.1, 0.1, None) == 3      # f32 source
+    assert f(p, p, p, p, p, 4, 2, 12, 16, 64, 2, 0.1, 0.1, None) == 3       # head_dim % 8
+    assert f(p, p, p, p, p, 4, 2, 128, 16, 64, 2, 0.0, 0.1, None) == 2      # scale must be > 0
+    assert f(p, p, p, p, p, 4, 2, 128, 16, 64, 2, 0.1, float("nan"), None) == 2
+    assert f(None, None, None, None, None, 0, 2, 128, 16, 64, 2, 0.1, 0.1, None) == 0
+    d = lib.pa_decode_fp8
+    args = [p, p, p, p, p, p, 4, 8, 2, 128, 16, 100, 8, 0.1, 2, 0.1, 0.1, 0, None, 0, 0, None]
+    def call(changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[k] = v
+        return d(*a)
+    assert call({0: None}) == 1
+    assert call({14: 0}) == 3               # f32 queries
+    assert call({14: 3}) == 3               # an 8-bit query type
+    assert call({9: 64}) == 3               # head_dim 64
+    assert call({20: 2}) == 3               # unknown flag
+    assert call({15: float("inf")}) == 2
+    assert call({12: 64, 17: 64}) == 4      # split needs a workspace
+    assert call({6: 0, 0: None}) == 0
+    c = lib.pa_copy_blocks
+    assert c(p, p, None, 1, 2, 64, 16, 64, 3, None) == 1   # 8-bit pools accepted (then null map)

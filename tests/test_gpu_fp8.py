@@ -1,0 +1,196 @@
+"""GPU parity of the 8-bit (E4M3) KV cache: pa_reshape_and_cache_fp8 bit-exact against the
+oracle's quantisation, pa_decode_fp8 against the float64 oracle on the dequantized pools
+(attention bar of ``gpu_helpers``: the quantisation is in the stored data, identical for both
+sides), and the block copies on 8-bit pools.  All calls go through the C ABI."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_05_amd import ops
+from paged_kv_cache_05_amd import workloads as W
+
+from gpu_helpers import assert_attention_close, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+K_SCALE = np.float32(W.FP8_DRAW_SCALE)       # pools drawn as N(0,1) / (1/64)
+V_SCALE = np.float32(W.FP8_DRAW_SCALE * 0.5)
+
+
+def _spec(dtype, bs, Hq, Hkv, lengths, seed, **kw):
+    kw.setdefault("new_tokens", ("free", 0))
+    return W.CaseSpec("fp8", seed, len(lengths), Hq, Hkv, 128, dtype, bs, ("fixed", list(lengths)),
+                      kv_dtype="fp8", **kw)
+
+
+def _upload(case, dev):
+    import torch
+    kc = W.to_torch(case.key_cache, "fp8", dev)
+    vc = W.to_torch(case.value_cache, "fp8", dev)
+    bt = torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).to(dev)
+    cl = torch.from_numpy(np.ascontiguousarray(case.context_lens, np.int32)).to(dev)
+    q = W.to_torch(case.query, case.dtype, dev)
+    return q, kc, vc, bt, cl
+
+
+def _vmax(case, vc=None):
+    vc = case.value_cache if vc is None else vc
+    m = 0.0
+    for s in range(case.spec.num_seqs):
+        n = int(case.context_lens[s])
+        if n > 0:
+            V = oracle.resolve_sequence(vc, case.block_tables[s], n, case.block_size, "f64")
+            m = max(m, float(np.nanmax(np.abs(V))))
+    return m
+
+
+def _oracle(case, kc=None, vc=None):
+    return oracle.decode_fp8_ref(case.query, case.key_cache if kc is None else kc,
+                                 case.value_cache if vc is None else vc, case.block_tables,
+                                 case.context_lens, case.block_size, case.scale, case.dtype,
+                                 K_SCALE, V_SCALE)
+
+
+MATRIX = [
+    ("bf16", 16, 8, 8, (1, 15, 16, 17, 200, 1000), 0),
+    ("f16", 16, 4, 4, (3, 64, 333, 70), 48),
+    ("bf16", 32, 8, 2, (1, 31, 500, 90), 0),          # GQA, 2 heads per workgroup
+    ("f16", 32, 6, 2, (40, 1, 129), 64),              # G = 3
+    ("bf16", 16, 4, 1, (2048, 1500), 256),            # G = 4, many partitions
+]
+
+
+@pytest.mark.parametrize("dtype,bs,Hq,Hkv,lengths,P", MATRIX)
+def test_decode_fp8_matches_oracle(dtype, bs, Hq, Hkv, lengths, P):
+    import torch
+    dev = need_gpu()
+    case = W.build_case(_spec(dtype, bs, Hq, Hkv, lengths, seed=200 + len(lengths) + bs + Hq))
+    say(f"decode_fp8 {dtype} bs{bs} Hq{Hq} Hkv{Hkv} lengths={lengths} P={P}")
+    q, kc, vc, bt, cl = _upload(case, dev)
+    out = torch.empty_like(q)
+    ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE),
+                   partition_size=P)
+    torch.cuda.synchronize()
+    got = W.from_torch(out, dtype)
+    vdeq = oracle.dequantize_fp8(case.value_cache, V_SCALE)
+    assert_attention_close(got, _oracle(case), dtype, _vmax(case, vdeq), "decode_fp8")
+
+
+def test_decode_fp8_poison_and_junk_tables():
+    import torch
+    dev = need_gpu()
+    spec = _spec("bf16", 16, 4, 4, (1, 15, 16, 33, 100), seed=210, max_blocks_per_seq=12)
+    outs = []
+    for kw in ({}, {"poison": True, "table_fill": -1}, {"poison": True, "table_fill": 2**31 - 1}):
+        case = W.build_case(spec, **kw)
+        q, kc, vc, bt, cl = _upload(case, dev)
+        out = torch.empty_like(q)
+        ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE))
+        torch.cuda.synchronize()
+        outs.append(W.from_torch(out, "bf16"))
+    assert np.all(np.isfinite(oracle.storage_to_f64(outs[0], "bf16")))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_reshape_and_cache_fp8_bit_exact(dtype):
+    """Quantised writes equal the oracle's bit for bit, including saturated values (inputs up
+    to ~40 / scale 0.05 = 800 > 448), skipped (-1) and out-of-pool slots."""
+    import torch
+    dev = need_gpu()
+    rng = np.random.default_rng(5)
+    NB, Hkv, bs, d, N = 40, 4, 16, 128, 37
+    kc0 = rng.integers(0, 0x7E, size=(NB, Hkv, bs, d), dtype=np.uint8)
+    vc0 = rng.integers(0, 0x7E, size=(NB, Hkv, bs, d), dtype=np.uint8)
+    key = W.round_to_storage(rng.standard_normal((N, Hkv, d)).astype(np.float32) * 10, dtype)
+    val = W.round_to_storage(rng.standard_normal((N, Hkv, d)).astype(np.float32) * 0.01, dtype)
+    slots = rng.choice(NB * bs, size=N, replace=False).astype(np.int64)
+    slots[3], slots[9] = -1, NB * bs + 5
+    ks, vs = np.float32(0.05), np.float32(1e-4)
+    want_k, want_v = oracle.reshape_and_cache_fp8_ref(key, val, kc0, vc0, slots, bs, dtype, ks, vs)
+    kc, vc = W.to_torch(kc0, "fp8", dev), W.to_torch(vc0, "fp8", dev)
+    ops.reshape_and_cache_fp8(W.to_torch(key, dtype, dev), W.to_torch(val, dtype, dev), kc, vc,
+                              torch.from_numpy(slots).to(dev), float(ks), float(vs))
+    torch.cuda.synchronize()
+    got_k, got_v = W.from_torch(kc, "fp8"), W.from_torch(vc, "fp8")
+    say(f"  reshape_fp8 {dtype}: saturated codes {int(np.sum((want_k & 0x7F) == 0x7E))}")
+    assert np.array_equal(got_k, want_k)
+    assert np.array_equal(got_v, want_v)
+
+
+def test_fp8_step_append_then_decode():
+    """reshape_and_cache_fp8 of each sequence's new token, then decode over the updated 8-bit
+    pools, against the oracle chain (quantise -> store -> dequantise -> attend)."""
+    import torch
+    dev = need_gpu()
+    spec = W.CaseSpec("fp8step", 220, 5, 8, 2, 128, "bf16", 16, ("fixed", [1, 16, 17, 300, 64]),
+                      kv_dtype="fp8")
+    case = W.build_case(spec)
+    q, kc, vc, bt, cl = _upload(case, dev)
+    nk, nv = W.to_torch(case.new_key, "bf16", dev), W.to_torch(case.new_value, "bf16", dev)
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    ops.reshape_and_cache_fp8(nk, nv, kc, vc, slots, float(K_SCALE), float(V_SCALE))
+    out = torch.empty_like(q)
+    ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE))
+    torch.cuda.synchronize()
+    k2, v2 = oracle.reshape_and_cache_fp8_ref(case.new_key, case.new_value, case.key_cache,
+                                              case.value_cache, case.slot_mapping, 16, "bf16",
+                                              K_SCALE, V_SCALE)
+    assert np.array_equal(W.from_torch(kc, "fp8"), k2)
+    ref = _oracle(case, k2, v2)
+    assert_attention_close(W.from_torch(out, "bf16"), ref, "bf16",
+                           _vmax(case, oracle.dequantize_fp8(v2, V_SCALE)), "fp8 step")
+
+
+def test_fp8_block_copies():
+    """copy_blocks and swap_blocks move 8-bit blocks bit for bit."""
+    import torch
+    dev = need_gpu()
+    rng = np.random.default_rng(7)
+    pool = rng.integers(0, 256, size=(20, 8, 16, 128), dtype=np.uint8)
+    kc, vc = W.to_torch(pool, "fp8", dev), W.to_torch(pool[::-1].copy(), "fp8", dev)
+    pairs = np.array([[1, 5], [7, 2], [19, 0]], np.int64)
+    ops.copy_blocks(kc, vc, torch.from_numpy(pairs).to(dev))
+    host_k = torch.zeros((6, 8, 16, 128), dtype=torch.uint8).pin_memory()
+    host_v = torch.zeros_like(host_k).pin_memory()
+    sw = np.array([[5, 0], [2, 3]], np.int64)
+    ops.swap_blocks(kc, vc, host_k, host_v, torch.from_numpy(sw).to(dev))
+    torch.cuda.synchronize()
+    wk, wv = oracle.copy_blocks_ref(pool, pool[::-1].copy(), pairs)
+    assert np.array_equal(W.from_torch(kc, "fp8"), wk)
+    assert np.array_equal(W.from_torch(vc, "fp8"), wv)
+    hk, hv = oracle.swap_blocks_ref(wk, wv, np.zeros((6, 8, 16, 128), np.uint8),
+                                    np.zeros((6, 8, 16, 128), np.uint8), sw)
+    assert np.array_equal(host_k.numpy(), hk) and np.array_equal(host_v.numpy(), hv)
+
+
+def test_decode_fp8_full_size_sampled():
+    """The Llama-7B-shaped workload over an 8-bit cache (pools drawn on the GPU), run as the
+    benchmark runs it; six sequences checked against the oracle."""
+    import torch
+    dev = need_gpu()
+    spec = W.CONFIGS["llama7b_bs16_fp8"]
+    case = W.build_case(spec, device=dev)
+    say(f"decode_fp8 full size: {case.num_blocks} blocks")
+    q = W.to_torch(case.query, "bf16", dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty_like(q)
+    ops.decode_fp8(out, q, case.key_cache, case.value_cache, bt, cl, float(case.scale),
+                   float(K_SCALE), float(V_SCALE))
+    torch.cuda.synchronize()
+    got = W.from_torch(out, "bf16")
+    for s in (0, 1, 77, 128, 200, 255):
+        n = int(case.context_lens[s])
+        nb = -(-n // 16)
+        ids = torch.from_numpy(case.block_tables[s, :nb].astype(np.int64)).to(dev)
+        kc = W.from_torch(case.key_cache.index_select(0, ids), "fp8")
+        vc = W.from_torch(case.value_cache.index_select(0, ids), "fp8")
+        ref = oracle.decode_fp8_ref(case.query[s:s + 1], kc, vc, np.arange(nb, dtype=np.int32)[None],
+                                    np.array([n], np.int32), 16, case.scale, "bf16", K_SCALE, V_SCALE)
+        vmax = float(np.max(np.abs(oracle.dequantize_fp8(vc, V_SCALE))))
+        assert_attention_close(got[s:s + 1], ref, "bf16", vmax, f"seq {s} (n={n})")
