@@ -10,8 +10,9 @@ kernel + log-sum-exp merge).  Inputs are seeded synthetic data drawn on the GPU 
 The reported value is the step's algorithmic bytes divided by the step time (GB/s).  The
 `roofline` object covers the dominant kernel (the decode partition kernel), timed with HIP
 events on the stream it runs on; `cpu_baseline` times the float64 CPU oracle on a bounded
-sample of the same workload.  `detail` adds the other decode workloads, swap_blocks over the
-host link and pa_prefill on two chunked-prefill workloads (matrix-core bound: TFLOP/s against
+sample of the same workload.  `detail` adds the other decode workloads (one over an 8-bit
+E4M3 cache: pa_reshape_and_cache_fp8 + pa_decode_fp8), swap_blocks over the host link and
+pa_prefill on two chunked-prefill workloads (matrix-core bound: TFLOP/s against
 the 2.5 PFLOP/s dense bf16 peak).  `--calibrate-copy` instead times copy_blocks on a known
 number of bytes (the reference copy used to scale hardware byte counters).
 """
@@ -56,8 +57,9 @@ def decode_bytes(case) -> int:
     table entries read and the context lengths."""
     sp = case.spec
     e = W.ELEM_BYTES[sp.dtype]
+    ekv = W.ELEM_BYTES[sp.kv_dtype or sp.dtype]
     n = case.context_lens.astype(np.int64)
-    kv = int(n.sum()) * sp.num_kv_heads * sp.head_dim * e * 2
+    kv = int(n.sum()) * sp.num_kv_heads * sp.head_dim * ekv * 2
     qo = sp.num_seqs * sp.num_heads * sp.head_dim * e * 2
     tables = int((-(-n // sp.block_size)).sum()) * 4 + 4 * sp.num_seqs
     return kv + qo + tables
@@ -66,15 +68,18 @@ def decode_bytes(case) -> int:
 def cache_write_bytes(case) -> int:
     sp = case.spec
     e = W.ELEM_BYTES[sp.dtype]
-    row = sp.num_kv_heads * sp.head_dim * e
-    reshape = len(case.slot_mapping) * (row * 2 * 2 + 8)               # read new K,V; write both
-    block = sp.num_kv_heads * sp.block_size * sp.head_dim * e
+    ekv = W.ELEM_BYTES[sp.kv_dtype or sp.dtype]
+    row = sp.num_kv_heads * sp.head_dim
+    reshape = len(case.slot_mapping) * (row * (e + ekv) * 2 + 8)       # read new K,V; write both
+    block = sp.num_kv_heads * sp.block_size * sp.head_dim * ekv
     copy = len(case.block_mapping) * (block * 2 * 2 + 16)               # read+write K and V blocks
     return reshape + copy
 
 
 def chosen_kernel(case, requested: str) -> str:
     sp = case.spec
+    if sp.kv_dtype == "fp8":
+        return "valu_fp8"
     if requested != "auto":
         return requested
     G = sp.num_heads // sp.num_kv_heads
@@ -99,6 +104,8 @@ class Step:
         self.out = torch.empty_like(self.q)
         self.P = sp.partition_size
         self.shared = bool(sp.shared_prefix)   # blocks read by several sequences of the call
+        self.fp8 = sp.kv_dtype == "fp8"        # 8-bit cache: pool scales as drawn
+        self.k_scale = self.v_scale = W.FP8_DRAW_SCALE
         nbytes = ops.workspace_bytes(sp.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim,
                                      sp.block_size, case.max_blocks_per_seq, self.P)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -106,12 +113,21 @@ class Step:
     def run(self, ev=None):
         if len(self.case.block_mapping):
             ops.copy_blocks(self.kc, self.vc, self.pairs)
-        ops.reshape_and_cache(self.nk, self.nv, self.kc, self.vc, self.slots)
+        if self.fp8:
+            ops.reshape_and_cache_fp8(self.nk, self.nv, self.kc, self.vc, self.slots,
+                                      self.k_scale, self.v_scale)
+        else:
+            ops.reshape_and_cache(self.nk, self.nv, self.kc, self.vc, self.slots)
         if ev is not None:
             ev[0].record()
-        ops.decode_partitions(self.out, self.q, self.kc, self.vc, self.bt, self.cl,
-                              float(self.case.scale), self.ws, partition_size=self.P,
-                              kernel=self.kernel, shared_blocks=self.shared)
+        if self.fp8:
+            ops.decode_fp8_partitions(self.out, self.q, self.kc, self.vc, self.bt, self.cl,
+                                      float(self.case.scale), self.k_scale, self.v_scale, self.ws,
+                                      partition_size=self.P, shared_blocks=self.shared)
+        else:
+            ops.decode_partitions(self.out, self.q, self.kc, self.vc, self.bt, self.cl,
+                                  float(self.case.scale), self.ws, partition_size=self.P,
+                                  kernel=self.kernel, shared_blocks=self.shared)
         if ev is not None:
             ev[1].record()
         ops.decode_merge(self.out, self.cl, self.case.spec.num_kv_heads, self.case.spec.block_size,
@@ -260,6 +276,12 @@ def prefill_flops(case) -> float:
     return 4.0 * case.spec.head_dim * case.spec.num_heads * pairs
 
 
+def _lengths_str(spec_lengths) -> str:
+    if spec_lengths[0] == "fixed" and len(set(spec_lengths[1])) == 1:
+        return f"{spec_lengths[1][0]} tokens each"
+    return str(spec_lengths)
+
+
 def measure_prefill(dev, name, steps, warmup):
     """pa_prefill on a chunked-prefill workload, both probability precisions, timed with HIP
     events on the launch stream."""
@@ -273,7 +295,7 @@ def measure_prefill(dev, name, steps, warmup):
     out = torch.empty_like(q)
     flops = prefill_flops(case)
     res = {"flops_per_launch": flops, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
-           "num_kv_heads": sp.num_kv_heads, "chunk": str(sp.chunk_lengths),
+           "num_kv_heads": sp.num_kv_heads, "chunk": _lengths_str(sp.chunk_lengths),
            "cached_prefix": str(sp.prefix_lengths)}
     for mode, bf16_p in (("p16", False), ("p_bf16", True)):
         def run():
@@ -311,7 +333,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
-    ap.add_argument("--also", default="llama7b_bs32,opt13b,gqa_long,shared_prefix",
+    ap.add_argument("--also", default="llama7b_bs32,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
