@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, AMD's published peak
 METRIC = "paged decode attention achieved HBM GB/s (% of MI355X peak) + seq-heads/s"
 TRAFFIC_FILE = ROOT / "profiles" / "decode_traffic.json"
 KERNEL_SOURCES = {
-    "valu": ["pa_decode_valu.hip", "pa_common.h"],
+    "valu": ["pa_decode_valu.h", "pa_decode_valu_bf16.hip", "pa_common.h"],
     "mfma": ["pa_decode_mfma.hip", "pa_common.h"],
 }
 

@@ -49,8 +49,8 @@ pa_status check_shape(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
                       int32_t partition_size) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || maxb <= 0 || partition_size < 0) return PA_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return PA_ERR_BAD_SHAPE;
-  if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
-  if (BS != 16 && BS != 32) return PA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 80 && D != 128 && D != 256) return PA_ERR_UNSUPPORTED;
+  if (BS != 16 && BS != 32 && BS != 64 && BS != 128) return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % BS != 0) return PA_ERR_BAD_SHAPE;
   if ((long)maxb * BS > (1L << 30)) return PA_ERR_BAD_SHAPE;
   return PA_OK;
@@ -67,7 +67,8 @@ int auto_partition(int32_t S, int32_t Hkv, int32_t BS, int32_t maxb) {
   const long parts = std::max(1L, (kTargetWorkgroups + units - 1) / units);
   long P = (cap + parts - 1) / parts;
   P = std::min<long>(std::max<long>(P, kMinPartition), kMaxPartition);
-  P = (P + 31) / 32 * 32;
+  const long q = std::max(32, (int)BS);   // partitions hold whole blocks
+  P = (P + q - 1) / q * q;
   if (P >= cap) return 0;  // one pass
   return (int)P;
 }
@@ -94,9 +95,14 @@ bool mfma_eligible(DT dt, int D, int G, int partition) {
   return (dt == DT::F16 || dt == DT::BF16) && D == 128 && G % 4 == 0 && partition % 16 == 0;
 }
 
-int heads_per_wg(bool mfma, int G) {
+// Query heads one workgroup serves.  The vector-ALU kernel keeps head_dim/64 .. head_dim/8
+// fp32 outputs per lane per head, so wide heads get fewer per workgroup.
+int heads_per_wg(bool mfma, int G, int D) {
   if (mfma) return G % 16 == 0 ? 16 : G % 8 == 0 ? 8 : 4;
-  return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  const int cap = D >= 256 ? 2 : D == 80 ? 4 : 8;
+  for (int gt = cap; gt > 1; gt /= 2)
+    if (G % gt == 0) return gt;
+  return 1;
 }
 
 pa_status launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
@@ -153,6 +159,7 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
     return PA_ERR_UNSUPPORTED;
   if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_UNSUPPORTED;
+  if (dt == DT::F32 && head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
@@ -172,7 +179,7 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   } else if (kernel == PA_KERNEL_AUTO) {
     mfma = can_mfma;
   }
-  const int gt = heads_per_wg(mfma, G);
+  const int gt = heads_per_wg(mfma, G, head_dim);
 
   pa::DecodeParams p;
   p.out = out;
@@ -423,7 +430,7 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
                             max_blocks_per_seq, partition_size);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return PA_ERR_WORKSPACE;
   const int G = num_heads / num_kv_heads;
-  const int gt = std::min(heads_per_wg(false, G), 2);   // 16 fp32 outputs per lane per head
+  const int gt = std::min(heads_per_wg(false, G, head_dim), 2);   // 16 fp32 outputs per lane per head
 
   pa::DecodeParams p;
   p.out = out;

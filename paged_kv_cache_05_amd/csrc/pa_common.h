@@ -240,6 +240,10 @@ struct PrefillParams {
 // host-side launchers (return hipSuccess or the launch error)
 hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
                               bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_valu_f16(int head_dim, int block_size, int heads_per_wg, bool stream_kv,
+                                  const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_valu_bf16(int head_dim, int block_size, int heads_per_wg, bool stream_kv,
+                                   const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_decode_valu_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
                                   bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_reshape_and_cache_fp8(DT dt, const void* key, const void* value, void* kc,

@@ -299,6 +299,8 @@ template <DT dt>
 hipError_t launch_bs(int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
   if (bs == 16) return sk ? launch_gt<dt, 16, true>(gt, p, grid, st) : launch_gt<dt, 16, false>(gt, p, grid, st);
   if (bs == 32) return sk ? launch_gt<dt, 32, true>(gt, p, grid, st) : launch_gt<dt, 32, false>(gt, p, grid, st);
+  if (bs == 64) return sk ? launch_gt<dt, 64, true>(gt, p, grid, st) : launch_gt<dt, 64, false>(gt, p, grid, st);
+  if (bs == 128) return sk ? launch_gt<dt, 128, true>(gt, p, grid, st) : launch_gt<dt, 128, false>(gt, p, grid, st);
   return hipErrorInvalidValue;
 }
 

@@ -1,4 +1,6 @@
-// Paged decode attention on the vector ALUs (gfx950, wave64).
+#pragma once
+// Paged decode attention on the vector ALUs (gfx950, wave64): the kernel template.  The
+// per-element-type files pa_decode_valu_*.hip instantiate it (in parallel translation units).
 //
 // What is computed: for one query per (sequence, head), softmax-weighted sum of V over the
 // sequence's cached tokens, with K/V fetched block by block through the block table (UltraLAB
@@ -18,7 +20,10 @@
 // its own online-softmax state (running max, denominator, partial output), so the loop has no
 // cross-row traffic.  Rows and waves are merged once, at the end of the partition.
 // The next chunk's K and V loads are issued before the current chunk is consumed.
+#include <type_traits>
+
 #include "pa_common.h"
+
 
 namespace pa {
 namespace {
@@ -29,12 +34,15 @@ struct ValuCfg {
   using Q = Elem<dt>;                        // query / output elements
   static constexpr int EPL = E::kPerVec;     // elements per lane per 16-byte vector
   static constexpr int QV = EPL / Q::kPerVec;  // query vectors per lane (2 for an 8-bit cache)
-  static constexpr int LPT = D / EPL;        // lanes per token row
+  static constexpr int VC = D / EPL;         // 16-byte vectors per token row
+  // lanes per token row: VC rounded up to a power of two (rows of 80 or 96 dims leave the
+  // last lanes of each row idle, so DPP reductions still run over a whole lane group)
+  static constexpr int LPT = VC <= 8 ? 8 : VC <= 16 ? 16 : 32;
   static constexpr int TPI = kWave / LPT;    // tokens per wave load instruction
   static constexpr int NI = 16 / TPI;        // load instructions per 16-token chunk
   static constexpr int CPB = BS / 16;        // chunks per block
   static constexpr int ROW_BYTES = D * E::kBytes;
-  static_assert(LPT >= 8 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "row must span 8..32 lanes");
+  static_assert(VC * EPL == D && VC >= 4 && VC <= 32, "row must be 4..32 whole vectors");
   static_assert(BS % 16 == 0, "block size must be a multiple of 16");
 };
 
@@ -44,11 +52,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   using E = typename C::E;
   using Q = typename C::Q;
   constexpr int EPL = C::EPL, LPT = C::LPT, TPI = C::TPI, NI = C::NI, CPB = C::CPB, QV = C::QV;
+  constexpr int VC = C::VC;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int row = lane / LPT;   // token slot inside one load instruction
   const int col = lane % LPT;   // 16-byte column of the token row
+  const bool act = col < VC;    // idle padding lanes (VC < LPT) read column VC-1, weight 0
+  const int colc = act ? col : VC - 1;
 
   // Workgroups are dealt round-robin to the 8 XCDs (id mod 8).  The partition index is the
   // slowest grid index so every XCD gets an even share of (sequence, head) units; with it
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
 #pragma unroll
     for (int v = 0; v < QV; ++v)
       qraw[h][v] = *reinterpret_cast<const uint4*>(
-          (const char*)p.q + (q_row0 + (size_t)h * D + col * EPL) * Q::kBytes + 16 * v);
+          (const char*)p.q + (q_row0 + (size_t)h * D + colc * EPL) * Q::kBytes + 16 * v);
   int ent_first = -1;
   {
     const int my_ch = ch_begin + wave + 4 * lane;
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   if (part >= nparts) return;
 
   if (n <= 0) {  // empty context: the output is defined as zero
-    if (wave == 0 && row == 0) {
+    if (wave == 0 && row == 0 && act) {
       const float z[EPL] = {};
 #pragma unroll
       for (int h = 0; h < GT; ++h)
@@ -104,6 +115,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   for (int h = 0; h < GT; ++h) {
 #pragma unroll
     for (int v = 0; v < QV; ++v) Q::unpack(qraw[h][v], qf[h] + v * Q::kPerVec);
+    if (!act) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] = 0.0f;
+    }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qf[h][e] *= p.scale_log2;
   }
@@ -121,7 +136,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int ch_end = (t_end + 15) / 16;
   const size_t head_off = (size_t)g * BS * D;               // elements
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
-  const int lane_off = (row * D + col * EPL) * E::kBytes;    // bytes inside a 16-token chunk
+  const int lane_off = (row * D + colc * EPL) * E::kBytes;   // bytes inside a 16-token chunk
 
   // address of this lane's first vector of chunk `ch` (physical block `phys`)
   auto chunk_ptr = [&](const void* base, int phys, int ch) -> const char* {
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   // merge the 4 waves through LDS
   __shared__ float s_o[4][GT][D];
   __shared__ float s_m[4][GT], s_l[4][GT];
-  if (row == 0) {
+  if (row == 0 && act) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
 #pragma unroll
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     }
   }
   __syncthreads();
-  if (threadIdx.x < GT * LPT) {
+  if (threadIdx.x < GT * LPT && (int)(threadIdx.x % LPT) < VC) {
     const int h = threadIdx.x / LPT, cc = threadIdx.x % LPT;
     float M = s_m[0][h];
 #pragma unroll
@@ -296,20 +311,31 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
 }
 
+// Heads per workgroup a (cache type, head dim) may use: each lane keeps EPL fp32 outputs per
+// head, and past ~64 of them occupancy drops to one wave per SIMD (or registers spill).
+template <DT kt, int D>
+constexpr int max_heads_per_wg() {
+  if constexpr (kt == DT::FP8 || D >= 256) return 2;
+  else if constexpr (D == 80 || D == 96) return 4;
+  else return 8;
+}
+
 template <DT dt, DT kt, int D, int BS, bool ST>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  constexpr int kMax = max_heads_per_wg<kt, D>();
+  if (gt > kMax) return hipErrorInvalidValue;
   switch (gt) {
     case 1: hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 1, ST>), dim3(grid), dim3(256), 0, st, p); break;
     case 2: hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 2, ST>), dim3(grid), dim3(256), 0, st, p); break;
     case 4:
+      if constexpr (kMax >= 4) {
+        hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     case 8:
-      // an 8-bit cache row gives each lane 16 elements: more than 2 heads per workgroup would
-      // hold 64+ fp32 outputs per lane and drop occupancy to one wave per SIMD
-      if constexpr (kt != DT::FP8) {
-        if (gt == 4)
-          hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p);
-        else
-          hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p);
+      if constexpr (kMax >= 8) {
+        hipLaunchKernelGGL((decode_valu_kernel<dt, kt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p);
         break;
       }
       return hipErrorInvalidValue;
@@ -318,49 +344,21 @@ hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <DT dt, DT kt, int D, int BS>
-hipError_t launch_st(bool stream_kv, int gt, const DecodeParams& p, int grid, hipStream_t st) {
-  return stream_kv ? launch_gt<dt, kt, D, BS, true>(gt, p, grid, st)
-                   : launch_gt<dt, kt, D, BS, false>(gt, p, grid, st);
-}
-
-template <DT dt>
-hipError_t launch_dt(int d, int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
-  if (d == 64 && bs == 16) return launch_st<dt, dt, 64, 16>(sk, gt, p, grid, st);
-  if (d == 64 && bs == 32) return launch_st<dt, dt, 64, 32>(sk, gt, p, grid, st);
-  if (d == 128 && bs == 16) return launch_st<dt, dt, 128, 16>(sk, gt, p, grid, st);
-  if (d == 128 && bs == 32) return launch_st<dt, dt, 128, 32>(sk, gt, p, grid, st);
-  return hipErrorInvalidValue;
-}
-
-template <DT dt>
-hipError_t launch_fp8(int d, int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
-  if (d == 128 && bs == 16) return launch_st<dt, DT::FP8, 128, 16>(sk, gt, p, grid, st);
-  if (d == 128 && bs == 32) return launch_st<dt, DT::FP8, 128, 32>(sk, gt, p, grid, st);
+template <DT dt, DT kt, int D>
+hipError_t launch_bs(int bs, int gt, bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
+  auto go = [&](auto bs_tag) -> hipError_t {
+    constexpr int BS = decltype(bs_tag)::value;
+    return stream_kv ? launch_gt<dt, kt, D, BS, true>(gt, p, grid, st)
+                     : launch_gt<dt, kt, D, BS, false>(gt, p, grid, st);
+  };
+  switch (bs) {
+    case 16: return go(std::integral_constant<int, 16>{});
+    case 32: return go(std::integral_constant<int, 32>{});
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 128: return go(std::integral_constant<int, 128>{});
+  }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
-
-hipError_t launch_decode_valu(DT dt, int head_dim, int block_size, int heads_per_wg,
-                              bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
-  switch (dt) {
-    case DT::F32: return launch_dt<DT::F32>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
-    case DT::F16: return launch_dt<DT::F16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
-    case DT::BF16: return launch_dt<DT::BF16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
-    default: break;
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_valu_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
-                                  bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
-  switch (dt) {
-    case DT::F16: return launch_fp8<DT::F16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
-    case DT::BF16: return launch_fp8<DT::BF16>(head_dim, block_size, heads_per_wg, stream_kv, p, grid, st);
-    default: break;
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace pa

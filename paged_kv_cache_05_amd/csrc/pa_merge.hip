@@ -26,8 +26,10 @@ template <> __device__ __forceinline__ void store_elem<DT::BF16>(void* out, size
 
 template <DT dt, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
-  constexpr int DPL = D / kWave;
+  constexpr int DPL = (D + kWave - 1) / kWave;   // dims per lane (80 dims: lanes 0..39 busy)
+  static_assert(D % DPL == 0, "whole lanes");
   const int lane = threadIdx.x & (kWave - 1);
+  const bool act = lane * DPL < D;
   const int idx = blockIdx.x * 4 + threadIdx.x / kWave;   // s * num_heads + h
   if (idx >= p.num_seqs * p.num_heads) return;
   const int s = idx / p.num_heads;
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   if (np <= 1) return;  // written directly by the decode kernel
 
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + (size_t)idx * p.max_parts;
-  const float* po = p.ws_o + (size_t)idx * p.max_parts * D + lane * DPL;
+  const float* po = p.ws_o + (size_t)idx * p.max_parts * D + (act ? lane * DPL : 0);
 
   float M = -INFINITY;
   for (int i = lane; i < np; i += kWave) M = fmaxf(M, ml[i].x);
@@ -76,6 +78,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
       }
     }
   }
+  if (!act) return;
   const float inv = 1.0f / L;
   const size_t obase = (size_t)idx * D + lane * DPL;
 #pragma unroll
@@ -86,12 +89,13 @@ template <DT dt>
 hipError_t launch_d(int d, const MergeParams& p, hipStream_t st) {
   const int grid = (p.num_seqs * p.num_heads + 3) / 4;
   if (grid == 0) return hipSuccess;
-  if (d == 64)
-    hipLaunchKernelGGL((merge_kernel<dt, 64>), dim3(grid), dim3(256), 0, st, p);
-  else if (d == 128)
-    hipLaunchKernelGGL((merge_kernel<dt, 128>), dim3(grid), dim3(256), 0, st, p);
-  else
-    return hipErrorInvalidValue;
+  switch (d) {
+    case 64: hipLaunchKernelGGL((merge_kernel<dt, 64>), dim3(grid), dim3(256), 0, st, p); break;
+    case 80: hipLaunchKernelGGL((merge_kernel<dt, 80>), dim3(grid), dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((merge_kernel<dt, 128>), dim3(grid), dim3(256), 0, st, p); break;
+    case 256: hipLaunchKernelGGL((merge_kernel<dt, 256>), dim3(grid), dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -102,6 +106,7 @@ hipError_t launch_merge(DT dt, int head_dim, const MergeParams& p, hipStream_t s
     case DT::F32: return launch_d<DT::F32>(head_dim, p, st);
     case DT::F16: return launch_d<DT::F16>(head_dim, p, st);
     case DT::BF16: return launch_d<DT::BF16>(head_dim, p, st);
+    default: break;
   }
   return hipErrorInvalidValue;
 }

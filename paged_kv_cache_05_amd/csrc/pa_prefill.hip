@@ -36,6 +36,8 @@
 // banks on both the stores and the MFMA operand reads):
 //   K tile  [64 tokens][16 chunks of 8 dims], chunk c of token t at slot c ^ (t & 15).
 //   V^T tile [128 dims][8 chunks of 8 token positions], chunk c of dim d at c ^ swz(d).
+#include <type_traits>
+
 #include "pa_common.h"
 
 namespace pa {
@@ -393,15 +395,22 @@ hipError_t go(const PrefillParams& p, int grid, hipStream_t st) {
 
 hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const PrefillParams& p,
                                int grid, hipStream_t st) {
-  if (dt == DT::BF16) {
-    if (!split_p) return block_size == 16 ? go<DT::BF16, 16, false>(p, grid, st)
-                                          : go<DT::BF16, 32, false>(p, grid, st);
-    return block_size == 16 ? go<DT::BF16, 16, true>(p, grid, st)
-                            : go<DT::BF16, 32, true>(p, grid, st);
-  }
-  if (dt == DT::F16)
-    return block_size == 16 ? go<DT::F16, 16, false>(p, grid, st)
-                            : go<DT::F16, 32, false>(p, grid, st);
+  auto by_bs = [&](auto dt_tag, auto split_tag) -> hipError_t {
+    constexpr DT T = decltype(dt_tag)::value;
+    constexpr bool SP = decltype(split_tag)::value;
+    switch (block_size) {
+      case 16: return go<T, 16, SP>(p, grid, st);
+      case 32: return go<T, 32, SP>(p, grid, st);
+      case 64: return go<T, 64, SP>(p, grid, st);
+      case 128: return go<T, 128, SP>(p, grid, st);
+    }
+    return hipErrorInvalidValue;
+  };
+  using BF = std::integral_constant<DT, DT::BF16>;
+  using HF = std::integral_constant<DT, DT::F16>;
+  if (dt == DT::BF16)
+    return split_p ? by_bs(BF{}, std::true_type{}) : by_bs(BF{}, std::false_type{});
+  if (dt == DT::F16) return by_bs(HF{}, std::false_type{});
   return hipErrorInvalidValue;
 }
 

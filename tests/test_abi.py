@@ -59,6 +59,8 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, scale=float("nan")) == 2
     assert _decode(lib, D=96) == 3                   # PA_ERR_UNSUPPORTED
     assert _decode(lib, BS=8) == 3
+    assert _decode(lib, D=80, dtype=0) == 3          # fp32 rows: head_dim 64 or 128 only
+    assert _decode(lib, D=256, BS=128, out=0) == 1   # 256 dims and 128-token blocks accepted
     assert _decode(lib, dtype=7) == 3
     assert _decode(lib, kernel=9) == 3
     assert _decode(lib, kernel=2, dtype=0) == 3      # matrix-core path needs f16/bf16

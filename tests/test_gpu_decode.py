@@ -50,6 +50,41 @@ def test_decode_matches_oracle(dtype, D, BS, kernel, partition):
     assert_attention_close(got, ref, dtype, live_vmax(c), f"{dtype}/{D}/{BS}/{kernel}/P{partition}")
 
 
+@pytest.mark.parametrize("BS", [64, 128])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_blocks(dtype, kernel, BS):
+    """Block sizes 64 and 128 (several 16-token chunks per block), single pass and split."""
+    dev = need_gpu()
+    Hq, Hkv = 8, 2
+    if kernel == "mfma" and dtype == "f32":
+        pytest.skip("matrix-core kernel needs f16/bf16")
+    say(f"decode {dtype} BS={BS} kernel={kernel}")
+    lengths = [1, BS - 1, BS, BS + 1, 3 * BS + 17, 700]
+    c = _case(dtype, 128, BS, Hq, Hkv, lengths=lengths, seed=BS + len(dtype))
+    u = Uploaded(c, dev)
+    for P in (0, BS, 2 * BS):
+        assert_attention_close(u.decode(kernel, P), oracle_decode(c), dtype, live_vmax(c),
+                               f"BS{BS}/{kernel}/P{P}")
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2), (4, 1)])
+@pytest.mark.parametrize("BS", [16, 64])
+@pytest.mark.parametrize("D", [80, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_head_dims_80_256(dtype, D, BS, heads):
+    """Head dims 80 (rows padded to 16 lanes, 6 idle) and 256 (32 lanes per row), with the
+    head groupings that give 1, 2 and 4 heads per workgroup."""
+    dev = need_gpu()
+    Hq, Hkv = heads
+    say(f"decode {dtype} D={D} BS={BS} Hq={Hq} Hkv={Hkv}")
+    c = _case(dtype, D, BS, Hq, Hkv, lengths=[1, 16, 65, 300, 1000], seed=D + BS + Hq)
+    u = Uploaded(c, dev)
+    for P in (0, 128):
+        assert_attention_close(u.decode("valu", P), oracle_decode(c), dtype, live_vmax(c),
+                               f"D{D}/BS{BS}/G{Hq // Hkv}/P{P}")
+
+
 @pytest.mark.parametrize("heads", [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1)])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_head_groupings(heads, kernel):

@@ -60,6 +60,8 @@ MATRIX = [
     ("bf16", 32, 8, 2, (1, 31, 500, 90), 0),          # GQA, 2 heads per workgroup
     ("f16", 32, 6, 2, (40, 1, 129), 64),              # G = 3
     ("bf16", 16, 4, 1, (2048, 1500), 256),            # G = 4, many partitions
+    ("bf16", 64, 8, 8, (1, 63, 64, 65, 700), 128),    # 64-token blocks
+    ("f16", 128, 4, 2, (1, 127, 129, 900), 0),        # 128-token blocks
 ]
 
 

@@ -83,6 +83,8 @@ MATRIX = [
     ("bf16", 16, 16, 2, (10, 0, 129), (20, 47, 9)),            # G = 8
     ("f16", 16, 6, 2, (0, 40, 5), (60, 23, 44)),               # G = 3 (not a power of two)
     ("bf16", 32, 2, 1, (0, 0), (300, 257)),                    # whole prompts, many tiles
+    ("bf16", 64, 4, 4, (0, 100, 63), (70, 129, 1)),             # 64-token blocks
+    ("f16", 128, 8, 2, (5, 300), (200, 1)),                     # 128-token blocks
 ]
 
 
