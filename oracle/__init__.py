@@ -5,6 +5,8 @@ Only the test-suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
 """
 
 from .pa_oracle import (  # noqa: F401
+    append_slots_ref,
+    block_hashes_ref,
     copy_blocks_ref,
     decode_ref,
     decode_fp8_ref,
@@ -12,6 +14,9 @@ from .pa_oracle import (  # noqa: F401
     dequantize_fp8,
     f64_to_fp8_e4m3,
     f64_to_storage,
+    fnv1a64,
+    fork_ref,
+    free_seqs_ref,
     fp8_e4m3_to_f64,
     kv_bytes_per_token,
     prefill_ref,

@@ -402,3 +402,138 @@ def decode_fp8_ref(query, key_cache, value_cache, block_tables, context_lens, bl
     vc = dequantize_fp8(value_cache, v_scale)
     qf = storage_to_f64(query, dtype)
     return decode_ref(qf, kc, vc, block_tables, context_lens, block_size, scale, "f64")
+
+
+# ---------------------------------------------------------------------------------------
+# block engine: append with copy-on-write, fork, free, prefix-block hashes
+# ---------------------------------------------------------------------------------------
+# The KV cache manager maps each sequence's logical blocks to physical blocks, allocates on
+# demand and reclaims freed blocks (xasun.com summary §二, block-engine item); shared blocks
+# carry reference counts and are copied before a sharer writes into them (same page, sharing
+# item).  The state below is the one the GPU keeps: tables, context lengths, one reference
+# count per block, and a stack of free block ids whose top ``free_top`` entries are free.
+def append_slots_ref(tables, ctx, refs, stack, free_top, seq_ids, block_size):
+    """Append one token to each listed sequence, in list order.
+
+    For a sequence with n tokens: if n is a multiple of the block size, a fresh block is taken
+    from the top of the free stack; else, if its last block is shared (reference count > 1),
+    a fresh block is taken, the pair (old, new) is recorded for copying, the old block loses a
+    reference and the table points at the new one; else the token goes into the last block.
+    The token's slot is block * bs + n mod bs, and n grows by one.  A sequence whose table is
+    full, or that needs a block when none is free, is left unchanged with slot -1 and raises
+    a status (1: out of blocks, 2: table full).
+
+    Returns (tables, ctx, refs, stack, free_top, slots, pairs, status), all copies."""
+    tables = np.array(tables, dtype=np.int32, copy=True)
+    ctx = np.array(ctx, dtype=np.int32, copy=True)
+    refs = np.array(refs, dtype=np.int32, copy=True)
+    stack = np.array(stack, dtype=np.int32, copy=True)
+    top = int(free_top)
+    bs = int(block_size)
+    slots, pairs, status = [], [], 0
+    for s in np.asarray(seq_ids, dtype=np.int64):
+        n = int(ctx[s])
+        j, off = divmod(n, bs)
+        if off == 0:
+            if j >= tables.shape[1]:
+                slots.append(-1)
+                status = max(status, 2)
+                continue
+            if top == 0:
+                slots.append(-1)
+                status = max(status, 1)
+                continue
+            top -= 1
+            new = int(stack[top])
+            tables[s, j] = new
+            refs[new] = 1
+            block = new
+        else:
+            block = int(tables[s, j])
+            if refs[block] > 1:
+                if top == 0:
+                    slots.append(-1)
+                    status = max(status, 1)
+                    continue
+                top -= 1
+                new = int(stack[top])
+                pairs.append((block, new))
+                refs[block] -= 1
+                refs[new] = 1
+                tables[s, j] = new
+                block = new
+        slots.append(block * bs + off)
+        ctx[s] = n + 1
+    return (tables, ctx, refs, stack, top, np.array(slots, np.int64),
+            np.array(pairs, np.int64).reshape(-1, 2), status)
+
+
+def fork_ref(tables, ctx, refs, parent_child, block_size):
+    """Each child gets the parent's table entries and length; every shared block gains one
+    reference (parallel sampling forks a sequence this way)."""
+    tables = np.array(tables, dtype=np.int32, copy=True)
+    ctx = np.array(ctx, dtype=np.int32, copy=True)
+    refs = np.array(refs, dtype=np.int32, copy=True)
+    for parent, child in np.asarray(parent_child, dtype=np.int64).reshape(-1, 2):
+        nb = num_blocks_for(int(ctx[parent]), block_size)
+        tables[child, :nb] = tables[parent, :nb]
+        ctx[child] = ctx[parent]
+        for b in tables[parent, :nb]:
+            refs[b] += 1
+    return tables, ctx, refs
+
+
+def free_seqs_ref(tables, ctx, refs, stack, free_top, seq_ids, block_size):
+    """Drop each listed sequence: every block loses a reference and blocks left with none go
+    back on the free stack (in table order, sequence by sequence); the length becomes 0 and
+    the freed table entries -1."""
+    tables = np.array(tables, dtype=np.int32, copy=True)
+    ctx = np.array(ctx, dtype=np.int32, copy=True)
+    refs = np.array(refs, dtype=np.int32, copy=True)
+    stack = np.array(stack, dtype=np.int32, copy=True)
+    top = int(free_top)
+    for s in np.asarray(seq_ids, dtype=np.int64):
+        nb = num_blocks_for(int(ctx[s]), block_size)
+        for j in range(nb):
+            b = int(tables[s, j])
+            refs[b] -= 1
+            if refs[b] == 0:
+                stack[top] = b
+                top += 1
+            tables[s, j] = -1
+        ctx[s] = 0
+    return tables, ctx, refs, stack, top
+
+
+_FNV_OFFSET = 0xCBF29CE484222325
+_FNV_PRIME = 0x100000001B3
+_MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data: bytes, h: int = _FNV_OFFSET) -> int:
+    """64-bit FNV-1a (Fowler, Noll, Vo): for each byte, h ^= byte, then h *= 2^40 + 2^8 + 0xb3
+    modulo 2^64, from the offset basis 0xcbf29ce484222325."""
+    for byte in data:
+        h ^= byte
+        h = (h * _FNV_PRIME) & _MASK64
+    return h
+
+
+def block_hashes_ref(token_ids, num_tokens, block_size) -> np.ndarray:
+    """Prefix hashes of full blocks, uint64 [S, max_tokens // bs]: block j's hash covers the
+    sequence's tokens 0 .. (j+1)*bs - 1, so two sequences share block j's hash exactly when
+    (up to collisions) they share that whole prefix, which is what lets a fixed system prompt's
+    blocks be reused (yongjin360.com §5.1, prefix caching).  g_j = FNV-1a-64 of the block's
+    token ids (int32, little-endian); h_j = FNV-1a-64 of the 16 bytes h_{j-1} || g_j
+    (little-endian, h_{-1} = 0).  Blocks that are not full get 0."""
+    tok = np.asarray(token_ids, dtype=np.int32)
+    S, T = tok.shape
+    bs = int(block_size)
+    out = np.zeros((S, T // bs), dtype=np.uint64)
+    for s in range(S):
+        h = 0
+        for j in range(int(num_tokens[s]) // bs):
+            g = fnv1a64(tok[s, j * bs:(j + 1) * bs].astype('<i4').tobytes())
+            h = fnv1a64(int(h).to_bytes(8, "little") + int(g).to_bytes(8, "little"))
+            out[s, j] = h
+    return out

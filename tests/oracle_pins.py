@@ -629,4 +629,132 @@ def pin_fp8_cache_and_decode(O):
         assert np.max(np.abs(out[s] - ref)) <= 1e-12, s
 
 
+# ---------------------------------------------------------------------------------------
+# block engine and prefix hashes
+# ---------------------------------------------------------------------------------------
+def _engine_state(O, NB=64, S=10, maxb=8, bs=4, seed=0):
+    """A random pool: sequences grown token by token through append_slots_ref, some forked."""
+    rng = np.random.default_rng(seed)
+    tables = np.full((S, maxb), -1, np.int32)
+    ctx = np.zeros(S, np.int32)
+    refs = np.zeros(NB, np.int32)
+    stack = rng.permutation(NB).astype(np.int32)
+    top = NB
+    live = list(range(S // 2))
+    for _ in range(25):                    # at most 25 tokens: tables (32 slots) never fill
+        seqs = rng.choice(live, size=rng.integers(1, len(live) + 1), replace=False)
+        tables, ctx, refs, stack, top, _, _, _ = O.append_slots_ref(tables, ctx, refs, stack, top, seqs, bs)
+    pc = np.array([[0, S // 2], [0, S // 2 + 1], [1, S // 2 + 2], [3, S // 2 + 3]], np.int64)
+    tables, ctx, refs = O.fork_ref(tables, ctx, refs, pc, bs)
+    return tables, ctx, refs, stack, top
+
+
+def _check_engine(tables, ctx, refs, stack, top, bs):
+    """Reference counts equal the number of table entries naming each block; the free stack's
+    live part and the referenced blocks partition the pool."""
+    NB = len(refs)
+    count = np.zeros(NB, np.int64)
+    for s in range(len(ctx)):
+        nb = -(-int(ctx[s]) // bs)
+        for b in tables[s, :nb]:
+            count[b] += 1
+    assert np.array_equal(count, refs), "reference counts"
+    free = set(int(b) for b in stack[:top])
+    used = set(np.flatnonzero(refs > 0).tolist())
+    assert len(free) == top and not (free & used) and (free | used) == set(range(NB)), "free list"
+
+
+def pin_block_engine_append(O):
+    """Appending through shared blocks: counts stay exact, the free list and the referenced
+    blocks partition the pool, every sequence still reads its old tokens (after the recorded
+    copies are applied to a content model) plus its new token in a block it alone holds, and
+    a shared last block is copied min(appenders, refs - 1) times."""
+    bs = 4
+    for seed in range(4):
+        tables, ctx, refs, stack, top = _engine_state(O, seed=seed)
+        _check_engine(tables, ctx, refs, stack, top, bs)
+        NB = len(refs)
+        content = {}                       # (block, offset) -> token label
+        for s in range(len(ctx)):
+            for t in range(int(ctx[s])):
+                content[(int(tables[s, t // bs]), t % bs)] = None
+        # label every slot by its physical position (values of the content model)
+        label = {k: k for k in content}
+        before = {s: [label[(int(tables[s, t // bs]), t % bs)] for t in range(int(ctx[s]))]
+                  for s in range(len(ctx))}
+        rng = np.random.default_rng(100 + seed)
+        seqs = rng.permutation(len(ctx))[: len(ctx) - 2]
+        last = {s: int(tables[s, (int(ctx[s]) - 1) // bs]) for s in seqs if ctx[s] % bs}
+        t2, c2, r2, st2, top2, slots, pairs, status = O.append_slots_ref(tables, ctx, refs, stack, top, seqs, bs)
+        assert status == 0
+        _check_engine(t2, c2, r2, st2, top2, bs)
+        model = dict(label)
+        for a, b in pairs:                 # copy-on-write: the whole block
+            for o in range(bs):
+                if (int(a), o) in label:
+                    model[(int(b), o)] = label[(int(a), o)]
+        for i, s in enumerate(seqs):
+            n = int(ctx[s])
+            assert c2[s] == n + 1
+            assert slots[i] == int(t2[s, n // bs]) * bs + n % bs
+            assert r2[int(t2[s, n // bs])] == 1, "the written block is private"
+            got = [model.get((int(t2[s, t // bs]), t % bs)) for t in range(n)]
+            assert got == before[s], "old tokens unchanged"
+        for b in set(last.values()):
+            appenders = sum(1 for v in last.values() if v == b)
+            copies = sum(1 for a, _ in pairs if a == b)
+            assert copies == min(appenders, int(refs[b]) - 1), (b, appenders, copies)
+        assert top - top2 == len(pairs) + sum(1 for s in seqs if ctx[s] % bs == 0)
+
+
+def pin_block_engine_fork_free(O):
+    """Forking a sequence and freeing the child restores the counts and the free set; freeing
+    every sequence returns every block to the free list; running out of blocks leaves the
+    sequence untouched with status 1."""
+    bs = 4
+    tables, ctx, refs, stack, top = _engine_state(O, seed=7)
+    t1, c1, r1 = O.fork_ref(tables, ctx, refs, np.array([[2, 9]], np.int64), bs)
+    assert c1[9] == ctx[2] and np.all(r1 >= refs)
+    t2, c2, r2, st2, top2 = O.free_seqs_ref(t1, c1, r1, stack, top, [9], bs)
+    assert np.array_equal(r2, refs) and top2 == top and c2[9] == 0
+    t3, c3, r3, st3, top3 = O.free_seqs_ref(tables, ctx, refs, stack, top, list(range(len(ctx))), bs)
+    assert top3 == len(refs) and np.all(r3 == 0) and sorted(st3.tolist()) == list(range(len(refs)))
+    # no free block left: a sequence needing one is skipped with status 1
+    full = np.array([0, 1], np.int32)
+    t4, c4, r4, st4, top4, slots, pairs, status = O.append_slots_ref(
+        np.array([[0, -1], [1, -1]], np.int32), np.array([4, 3], np.int32), np.array([1, 1], np.int32),
+        full, 0, [0, 1], 4)
+    assert status == 1 and slots[0] == -1 and c4[0] == 4 and slots[1] == 1 * 4 + 3 and c4[1] == 4
+
+
+def pin_fnv_vectors(O):
+    """FNV-1a 64-bit check values of the published algorithm: "", "a", "foobar"."""
+    assert O.fnv1a64(b"") == 0xCBF29CE484222325
+    assert O.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert O.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def pin_block_hashes(O):
+    """Block j's hash depends on exactly tokens 0 .. (j+1)bs-1: sequences with a common prefix
+    share the hashes of the blocks inside it and differ afterwards; changing one token changes
+    its block's hash and every later one only; blocks that are not full hash to 0; hashes
+    chain h_j = FNV(h_{j-1} || g_j) (checked for two blocks by hand)."""
+    rng = np.random.default_rng(9)
+    bs, T = 4, 24
+    base = rng.integers(0, 50000, size=T, dtype=np.int32)
+    tok = np.stack([base, base, base, base])
+    tok[1, 13] += 1                       # differs in block 3
+    tok[2, 0] += 7                        # differs from the start
+    lens = np.array([24, 24, 24, 10], np.int32)
+    h = O.block_hashes_ref(tok, lens, bs)
+    assert np.array_equal(h[1, :3], h[0, :3]) and np.all(h[1, 3:] != h[0, 3:])
+    assert np.all(h[2] != h[0])
+    assert np.array_equal(h[3, :2], h[0, :2]) and np.all(h[3, 2:] == 0)
+    g0 = O.fnv1a64(base[:4].astype("<i4").tobytes())
+    h0 = O.fnv1a64((0).to_bytes(8, "little") + g0.to_bytes(8, "little"))
+    g1 = O.fnv1a64(base[4:8].astype("<i4").tobytes())
+    h1 = O.fnv1a64(h0.to_bytes(8, "little") + g1.to_bytes(8, "little"))
+    assert int(h[0, 0]) == h0 and int(h[0, 1]) == h1
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

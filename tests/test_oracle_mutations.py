@@ -68,6 +68,16 @@ MUTATIONS = [
     ("fp8 no saturation", "    y = np.clip(y, np.float32(-FP8_MAX), np.float32(FP8_MAX))\n", ""),
     ("fp8 scale multiplies", "inv = np.float32(1.0) / np.float32(scale)", "inv = np.float32(scale)"),
     ("fp8 value scale for keys", "    kc = dequantize_fp8(key_cache, k_scale)", "    kc = dequantize_fp8(key_cache, v_scale)"),
+    ("CoW on any reference", "            if refs[block] > 1:", "            if refs[block] >= 1:"),
+    ("CoW keeps the old reference", "                refs[block] -= 1\n", "                pass\n"),
+    ("fresh block unreferenced", "            tables[s, j] = new\n            refs[new] = 1\n", "            tables[s, j] = new\n"),
+    ("append slot offset", "        slots.append(block * bs + off)", "        slots.append(block * bs + off + 1)"),
+    ("fork without reference", "        for b in tables[parent, :nb]:\n            refs[b] += 1", "        for b in tables[parent, :nb]:\n            pass"),
+    ("free pushes shared blocks", "            if refs[b] == 0:\n                stack[top] = b", "            if refs[b] <= 1:\n                stack[top] = b"),
+    ("FNV prime", "_FNV_PRIME = 0x100000001B3", "_FNV_PRIME = 0x100000001B5"),
+    ("FNV order", "        h ^= byte\n        h = (h * _FNV_PRIME) & _MASK64", "        h = (h * _FNV_PRIME) & _MASK64\n        h ^= byte"),
+    ("hash chain ignores the prefix", "            h = fnv1a64(int(h).to_bytes(8, \"little\") + int(g).to_bytes(8, \"little\"))",
+     "            h = fnv1a64(int(0).to_bytes(8, \"little\") + int(g).to_bytes(8, \"little\"))"),
 ]
 
 
