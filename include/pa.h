@@ -319,6 +319,82 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
                                    void* workspace, size_t workspace_bytes, uint32_t flags,
                                    void* stream);
 
+/*
+ * Block engine on the device.  The KV cache manager maps each sequence's logical blocks to
+ * physical ones, allocates on demand and reclaims (xasun.com summary §二, block-engine item);
+ * shared blocks carry reference counts and are copied before a sharer writes (same page,
+ * sharing item).  These entry points keep that state in caller-owned device arrays so a
+ * decode step's slots and copy pairs are produced on the GPU:
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ *   ref_counts    int32 [num_blocks]: how many table entries name each block
+ *   free_stack    int32 [num_blocks]; free_top int32 [1]: free_stack[0 .. *free_top-1] are
+ *                 the free blocks (the top entry is taken first)
+ * Calls on one stream see each other's updates in order; calls that overlap on the same
+ * state race.
+ *
+ * pa_append_slots — append one token to each sequence seq_ids[i] (distinct ids).  With n its
+ * length: if n is a multiple of block_size, a free block is taken for the token; else if its
+ * last block is shared (reference count > 1), a free block is taken, the pair (old, new) is
+ * appended to block_mapping (int64 [num_append][2]; *num_pairs counts them), the old block
+ * loses a reference and the table points at the new one; else the token goes into the last
+ * block.  slot_mapping[i] (int64) = block * block_size + n % block_size and the length grows
+ * by one.  The outcome equals some one-at-a-time order of the sequences (which free block a
+ * sequence receives, and which sharer keeps a shared block, may differ between runs).  A
+ * sequence that cannot append gets slot -1, keeps its state, and raises *status (int32,
+ * device): 1 no free block, 2 table full, 3 a sequence or block id outside its array; 0 if
+ * all appended.  *num_pairs and *status are always written, also for num_append = 0.
+ */
+pa_status pa_append_slots(int32_t* block_tables, int32_t* context_lens, int32_t* ref_counts,
+                          int32_t* free_stack, int32_t* free_top, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                          const int32_t* seq_ids, int32_t num_append, int64_t* slot_mapping,
+                          int64_t* block_mapping, int32_t* num_pairs, int32_t* status,
+                          void* stream);
+
+/*
+ * pa_fork_seqs — for each (parent, child) row of parent_child (int32 [num_forks][2]), the
+ * child gets the parent's table entries and length and every block of the parent gains one
+ * reference (parallel sampling).  Children must be distinct, hold no blocks, and not be
+ * parents in the same call.
+ */
+pa_status pa_fork_seqs(int32_t* block_tables, int32_t* context_lens, int32_t* ref_counts,
+                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t num_blocks, const int32_t* parent_child, int32_t num_forks,
+                       void* stream);
+
+/*
+ * pa_free_seqs — drop each sequence seq_ids[i] (distinct): every block loses a reference,
+ * blocks left with none are pushed on the free stack (in no particular order), the table
+ * entries become -1 and the length 0.
+ */
+pa_status pa_free_seqs(int32_t* block_tables, int32_t* context_lens, int32_t* ref_counts,
+                       int32_t* free_stack, int32_t* free_top, int32_t num_seqs,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                       const int32_t* seq_ids, int32_t num_free, void* stream);
+
+/*
+ * pa_copy_blocks_counted — pa_copy_blocks with the pair count read on the device
+ * (*num_pairs, as pa_append_slots writes it); max_pairs bounds it and sizes the launch.
+ */
+pa_status pa_copy_blocks_counted(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                                 const int32_t* num_pairs, int32_t max_pairs,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * pa_block_hashes — prefix hashes of full blocks, so blocks of a common prompt prefix (a
+ * fixed system prompt: yongjin360.com page §5.1, prefix caching) can be recognised:
+ *   g_j = FNV-1a-64 of the block's block_size token ids (int32, little-endian bytes),
+ *   h_j = FNV-1a-64 of the 16 bytes h_{j-1} || g_j (little-endian; h_{-1} = 0),
+ * so h_j depends on exactly the tokens 0 .. (j+1)*block_size - 1.
+ *   token_ids  int32 [num_seqs][max_tokens]; num_tokens int32 [num_seqs]
+ *   hashes     uint64 [num_seqs][max_tokens / block_size] (written; 0 for blocks not full)
+ */
+pa_status pa_block_hashes(const int32_t* token_ids, const int32_t* num_tokens, int32_t num_seqs,
+                          int32_t max_tokens, int32_t block_size, uint64_t* hashes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,6 +107,24 @@ int heads_per_wg(bool mfma, int G, int D) {
 
 pa_status launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// Device block-engine state from the ABI arguments.
+pa_status engine_of(int32_t* tables, int32_t* lens, int32_t* refs, int32_t* stack, int32_t* top,
+                    int32_t num_seqs, int32_t maxb, int32_t bs, int32_t num_blocks,
+                    bool needs_stack, pa::EngineState* e) {
+  if (num_seqs < 0 || maxb <= 0 || bs <= 0 || num_blocks <= 0) return PA_ERR_BAD_SHAPE;
+  if (!tables || !lens || !refs || (needs_stack && (!stack || !top))) return PA_ERR_NULL_PTR;
+  e->tables = tables;
+  e->context_lens = lens;
+  e->ref_counts = refs;
+  e->free_stack = stack;
+  e->free_top = top;
+  e->num_seqs = num_seqs;
+  e->max_blocks_per_seq = maxb;
+  e->block_size = bs;
+  e->num_blocks = num_blocks;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -477,6 +495,90 @@ pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
   return pa_decode_merge(out, context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
                          block_size, max_blocks_per_seq, dtype, partition_size, workspace,
                          workspace_bytes, stream);
+}
+
+
+pa_status pa_append_slots(int32_t* block_tables, int32_t* context_lens, int32_t* ref_counts,
+                          int32_t* free_stack, int32_t* free_top, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                          const int32_t* seq_ids, int32_t num_append, int64_t* slot_mapping,
+                          int64_t* block_mapping, int32_t* num_pairs, int32_t* status,
+                          void* stream) {
+  pa::EngineState e;
+  pa_status st = engine_of(block_tables, context_lens, ref_counts, free_stack, free_top, num_seqs,
+                           max_blocks_per_seq, block_size, num_blocks, true, &e);
+  if (st != PA_OK) return st;
+  if (num_append < 0) return PA_ERR_BAD_SHAPE;
+  if (!num_pairs || !status) return PA_ERR_NULL_PTR;
+  if (num_append > 0 && (!seq_ids || !slot_mapping || !block_mapping)) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_append_slots(e, seq_ids, num_append, slot_mapping,
+                                               block_mapping, num_pairs, status,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_fork_seqs(int32_t* block_tables, int32_t* context_lens, int32_t* ref_counts,
+                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t num_blocks, const int32_t* parent_child, int32_t num_forks,
+                       void* stream) {
+  pa::EngineState e;
+  pa_status st = engine_of(block_tables, context_lens, ref_counts, nullptr, nullptr, num_seqs,
+                           max_blocks_per_seq, block_size, num_blocks, false, &e);
+  if (st != PA_OK) return st;
+  if (num_forks < 0) return PA_ERR_BAD_SHAPE;
+  if (num_forks == 0) return PA_OK;
+  if (!parent_child) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_fork(e, parent_child, num_forks,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_free_seqs(int32_t* block_tables, int32_t* context_lens, int32_t* ref_counts,
+                       int32_t* free_stack, int32_t* free_top, int32_t num_seqs,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                       const int32_t* seq_ids, int32_t num_free, void* stream) {
+  pa::EngineState e;
+  pa_status st = engine_of(block_tables, context_lens, ref_counts, free_stack, free_top, num_seqs,
+                           max_blocks_per_seq, block_size, num_blocks, true, &e);
+  if (st != PA_OK) return st;
+  if (num_free < 0) return PA_ERR_BAD_SHAPE;
+  if (num_free == 0) return PA_OK;
+  if (!seq_ids) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_free_seqs(e, seq_ids, num_free,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks_counted(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                                 const int32_t* num_pairs, int32_t max_pairs,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pa_dtype dtype, void* stream) {
+  DT dt;
+  if (!pool_dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
+  if (max_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  const long block_bytes = (long)num_kv_heads * block_size * head_dim * elem_bytes(dt);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (max_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_mapping || !num_pairs) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_block_copy(key_cache, value_cache, key_cache, value_cache,
+                                             block_mapping, max_pairs, block_bytes / 16,
+                                             num_blocks, num_blocks,
+                                             reinterpret_cast<hipStream_t>(stream), num_pairs));
+}
+
+pa_status pa_block_hashes(const int32_t* token_ids, const int32_t* num_tokens, int32_t num_seqs,
+                          int32_t max_tokens, int32_t block_size, uint64_t* hashes,
+                          void* stream) {
+  if (num_seqs < 0 || max_tokens < 0 || block_size <= 0 || block_size > 4096)
+    return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || max_tokens < block_size) return PA_OK;
+  if (!token_ids || !num_tokens || !hashes) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_block_hashes(token_ids, num_tokens, num_seqs, max_tokens,
+                                               block_size, hashes,
+                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -80,10 +80,12 @@ __global__ __launch_bounds__(256) void block_copy_kernel(const uint4* __restrict
                                                          uint4* __restrict__ dst_v,
                                                          const int64_t* __restrict__ mapping,
                                                          int64_t block_vecs, int chunks,
-                                                         int src_blocks, int dst_blocks) {
+                                                         int src_blocks, int dst_blocks,
+                                                         const int32_t* __restrict__ count) {
   const int chunk = blockIdx.x % chunks;
   const int which = (blockIdx.x / chunks) & 1;
   const int pair = blockIdx.x / (2 * chunks);
+  if (count != nullptr && pair >= *count) return;   // pair count produced on the device
   const int64_t src = mapping[2 * pair], dst = mapping[2 * pair + 1];
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const uint4* s = (which ? src_v : src_k) + src * block_vecs;
@@ -138,14 +140,15 @@ hipError_t launch_reshape_and_cache_fp8(DT dt, const void* key, const void* valu
 
 hipError_t launch_block_copy(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
                              const int64_t* mapping, int num_pairs, int64_t block_vecs,
-                             int src_blocks, int dst_blocks, hipStream_t st) {
+                             int src_blocks, int dst_blocks, hipStream_t st,
+                             const int32_t* count) {
   if (num_pairs <= 0) return hipSuccess;
   const int chunks = (int)((block_vecs + kCopyVecsPerWg - 1) / kCopyVecsPerWg);
   const int64_t grid = (int64_t)num_pairs * 2 * chunks;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)grid), dim3(256), 0, st,
                      (const uint4*)src_k, (const uint4*)src_v, (uint4*)dst_k, (uint4*)dst_v,
-                     mapping, block_vecs, chunks, src_blocks, dst_blocks);
+                     mapping, block_vecs, chunks, src_blocks, dst_blocks, count);
   return hipGetLastError();
 }
 

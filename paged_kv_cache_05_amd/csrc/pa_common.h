@@ -260,8 +260,26 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
                                     const int64_t* slots, int num_tokens, int row_vecs,
                                     int block_size, int num_blocks, int num_kv_heads,
                                     hipStream_t st);
+// `count` (device, optional): only pairs below *count are copied (num_pairs bounds the grid)
 hipError_t launch_block_copy(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
                              const int64_t* mapping, int num_pairs, int64_t block_vecs,
-                             int src_blocks, int dst_blocks, hipStream_t st);
+                             int src_blocks, int dst_blocks, hipStream_t st,
+                             const int32_t* count = nullptr);
+
+struct EngineState {           // block-engine state kept on the device (all caller-owned)
+  int32_t* tables;             // [num_seqs][max_blocks_per_seq]
+  int32_t* context_lens;       // [num_seqs]
+  int32_t* ref_counts;         // [num_blocks]
+  int32_t* free_stack;         // [num_blocks]; entries below *free_top are free blocks
+  int32_t* free_top;           // [1]
+  int32_t num_seqs, max_blocks_per_seq, block_size, num_blocks;
+};
+hipError_t launch_append_slots(const EngineState& e, const int32_t* seq_ids, int n,
+                               int64_t* slots, int64_t* pairs, int32_t* num_pairs,
+                               int32_t* status, hipStream_t st);
+hipError_t launch_fork(const EngineState& e, const int32_t* parent_child, int n, hipStream_t st);
+hipError_t launch_free_seqs(const EngineState& e, const int32_t* seq_ids, int n, hipStream_t st);
+hipError_t launch_block_hashes(const int32_t* tokens, const int32_t* num_tokens, int num_seqs,
+                               int max_tokens, int block_size, uint64_t* hashes, hipStream_t st);
 
 }  // namespace pa

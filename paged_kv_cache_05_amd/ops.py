@@ -46,6 +46,11 @@ _SIGNATURES = {
     "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
     "pa_swap_blocks": (_c_int, [_p, _p, _c_int, _p, _p, _c_int, _p] + [_c_int] * 5 + [_p]),
     "pa_prefill": (_c_int, [_p] * 7 + [_c_int] * 8 + [_c_float, _c_int, ctypes.c_uint32, _p]),
+    "pa_append_slots": (_c_int, [_p] * 5 + [_c_int] * 4 + [_p, _c_int] + [_p] * 4 + [_p]),
+    "pa_fork_seqs": (_c_int, [_p] * 3 + [_c_int] * 4 + [_p, _c_int, _p]),
+    "pa_free_seqs": (_c_int, [_p] * 5 + [_c_int] * 4 + [_p, _c_int, _p]),
+    "pa_copy_blocks_counted": (_c_int, [_p] * 4 + [_c_int] * 6 + [_p]),
+    "pa_block_hashes": (_c_int, [_p, _p] + [_c_int] * 3 + [_p, _p]),
     "pa_reshape_and_cache_fp8": (_c_int, [_p] * 5 + [_c_int] * 6 + [_c_float, _c_float, _p]),
     "pa_decode_fp8": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_float, _c_float,
                                                       _c_int, _p, _c_size, ctypes.c_uint32, _p]),
@@ -377,3 +382,81 @@ def decode_fp8_partitions(out, query, key_cache, value_cache, block_tables, cont
                                            _ptr(workspace), wsb,
                                            PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                            _stream(dev, stream)), "pa_decode_fp8_partitions")
+
+
+# ---------------------------------------------------------------------------------------
+# block engine on the device
+# ---------------------------------------------------------------------------------------
+def _engine(block_tables, context_lens, ref_counts, free_stack=None, free_top=None):
+    import torch
+    for t in (block_tables, context_lens, ref_counts, free_stack, free_top):
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError("block-engine arrays are int32")
+    if block_tables.dim() != 2 or context_lens.shape != (block_tables.shape[0],):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens [num_seqs]")
+    if free_stack is not None and free_stack.shape != ref_counts.shape:
+        raise ValueError("free_stack must have one entry per block")
+    return block_tables.shape[0], block_tables.shape[1], ref_counts.numel()
+
+
+def append_slots(block_tables, context_lens, ref_counts, free_stack, free_top, seq_ids, block_size,
+                 slot_mapping, block_mapping, num_pairs, status, *, stream=None):
+    """pa_append_slots: one token per sequence in seq_ids (int32), with copy-on-write; writes
+    slot_mapping (int64 [n]), block_mapping (int64 [n, 2]), num_pairs and status (int32 [1])."""
+    import torch
+    dev = _dev(block_tables, context_lens, ref_counts, free_stack, free_top, seq_ids, slot_mapping,
+               block_mapping, num_pairs, status)
+    S, maxb, NB = _engine(block_tables, context_lens, ref_counts, free_stack, free_top)
+    n = seq_ids.numel()
+    if slot_mapping.dtype != torch.int64 or block_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping and block_mapping are int64")
+    if slot_mapping.numel() < n or block_mapping.numel() < 2 * n:
+        raise ValueError("slot_mapping [n] and block_mapping [n, 2] needed")
+    _check(load().pa_append_slots(_ptr(block_tables), _ptr(context_lens), _ptr(ref_counts),
+                                  _ptr(free_stack), _ptr(free_top), S, maxb, int(block_size), NB,
+                                  _ptr(seq_ids), n, _ptr(slot_mapping), _ptr(block_mapping),
+                                  _ptr(num_pairs), _ptr(status), _stream(dev, stream)),
+           "pa_append_slots")
+
+
+def fork_seqs(block_tables, context_lens, ref_counts, parent_child, block_size, *, stream=None):
+    """pa_fork_seqs: parent_child int32 [n, 2]."""
+    dev = _dev(block_tables, context_lens, ref_counts, parent_child)
+    S, maxb, NB = _engine(block_tables, context_lens, ref_counts)
+    _check(load().pa_fork_seqs(_ptr(block_tables), _ptr(context_lens), _ptr(ref_counts), S, maxb,
+                               int(block_size), NB, _ptr(parent_child), parent_child.shape[0],
+                               _stream(dev, stream)), "pa_fork_seqs")
+
+
+def free_seqs(block_tables, context_lens, ref_counts, free_stack, free_top, seq_ids, block_size, *,
+              stream=None):
+    """pa_free_seqs: seq_ids int32 [n]."""
+    dev = _dev(block_tables, context_lens, ref_counts, free_stack, free_top, seq_ids)
+    S, maxb, NB = _engine(block_tables, context_lens, ref_counts, free_stack, free_top)
+    _check(load().pa_free_seqs(_ptr(block_tables), _ptr(context_lens), _ptr(ref_counts),
+                               _ptr(free_stack), _ptr(free_top), S, maxb, int(block_size), NB,
+                               _ptr(seq_ids), seq_ids.numel(), _stream(dev, stream)), "pa_free_seqs")
+
+
+def copy_blocks_counted(key_cache, value_cache, block_mapping, num_pairs, max_pairs, *, stream=None):
+    """pa_copy_blocks_counted: the pair count is read from num_pairs (int32 [1], on the GPU)."""
+    dev = _dev(key_cache, value_cache, block_mapping, num_pairs)
+    NB, Hkv, BS, D = key_cache.shape
+    _check(load().pa_copy_blocks_counted(_ptr(key_cache), _ptr(value_cache), _ptr(block_mapping),
+                                         _ptr(num_pairs), int(max_pairs), Hkv, D, BS, NB,
+                                         _dtype_code(key_cache), _stream(dev, stream)),
+           "pa_copy_blocks_counted")
+
+
+def block_hashes(token_ids, num_tokens, block_size, hashes, *, stream=None):
+    """pa_block_hashes: token_ids int32 [S, T], num_tokens int32 [S] -> hashes [S, T // bs]
+    (a 64-bit tensor; the bits are the unsigned FNV-1a values)."""
+    import torch
+    dev = _dev(token_ids, num_tokens, hashes)
+    S, T = token_ids.shape
+    if token_ids.dtype != torch.int32 or num_tokens.dtype != torch.int32:
+        raise TypeError("token_ids and num_tokens are int32")
+    if hashes.element_size() != 8 or tuple(hashes.shape) != (S, T // int(block_size)):
+        raise ValueError("hashes must be 64-bit [num_seqs, max_tokens // block_size]")
+    _check(load().pa_block_hashes(_ptr(token_ids), _ptr(num_tokens), S, T, int(block_size),
+                                  _ptr(hashes), _stream(dev, stream)), "pa_block_hashes")

@@ -170,3 +170,25 @@ def test_fp8_argument_errors(lib):
     assert call({6: 0, 0: None}) == 0
     c = lib.pa_copy_blocks
     assert c(p, p, None, 1, 2, 64, 16, 64, 3, None) == 1   # 8-bit pools accepted (then null map)
+
+
+def test_block_engine_argument_errors(lib):
+    p = ctypes.c_void_p(1)
+    a = lib.pa_append_slots
+    assert a(p, p, p, p, None, 4, 8, 16, 64, p, 2, p, p, p, p, None) == 1      # no free_top
+    assert a(p, p, p, p, p, 4, 8, 16, 64, p, 2, p, p, None, p, None) == 1      # no counter
+    assert a(p, p, p, p, p, 4, 0, 16, 64, p, 2, p, p, p, p, None) == 2         # no table width
+    assert a(p, p, p, p, p, 4, 8, 16, 64, p, -1, p, p, p, p, None) == 2
+    f = lib.pa_fork_seqs
+    assert f(p, p, p, 4, 8, 16, 64, None, 2, None) == 1
+    assert f(p, p, p, 4, 8, 16, 64, None, 0, None) == 0
+    r = lib.pa_free_seqs
+    assert r(p, p, p, None, p, 4, 8, 16, 64, p, 1, None) == 1
+    assert r(p, p, p, p, p, 4, 8, 16, 64, None, 0, None) == 0
+    c = lib.pa_copy_blocks_counted
+    assert c(p, p, p, None, 4, 2, 64, 16, 64, 1, None) == 1
+    assert c(p, p, p, p, 0, 2, 64, 16, 64, 1, None) == 0
+    h = lib.pa_block_hashes
+    assert h(p, p, 4, 64, 0, p, None) == 2
+    assert h(p, None, 4, 64, 16, p, None) == 1
+    assert h(None, None, 4, 8, 16, None, None) == 0                            # no full block
