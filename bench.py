@@ -318,6 +318,74 @@ def measure_prefill(dev, name, steps, warmup):
     return res
 
 
+def measure_device_engine(dev, steps, warmup):
+    """The shared-prefix step with its bookkeeping on the GPU: pa_append_slots (one token for
+    each of the 64 sequences, copy-on-write where a forked sibling shares the last block) ->
+    pa_copy_blocks_counted (device pair count) -> reshape_and_cache at the device-made slots ->
+    decode.  Reports the append and counted-copy launches and the whole step."""
+    import torch
+    case = W.build_case(W.CONFIGS["shared_prefix"], device=dev)
+    sp = case.spec
+    S, NB, bs = sp.num_seqs, case.num_blocks, sp.block_size
+    # engine state before the step: the sequences (lengths without the step's token) and their
+    # forked siblings; reference counts = table entries naming each block
+    lens = case.context_lens.astype(np.int64) - 1
+    tables = np.concatenate([case.block_tables, case.sibling_tables]).astype(np.int32)
+    ctx = np.concatenate([lens, case.sibling_lens]).astype(np.int32)
+    pre = case.block_tables.copy()
+    for s in range(S):                       # undo the step's own copy-on-write / new block
+        nb_old = -(-int(lens[s]) // bs)
+        pre[s, nb_old:] = -1
+        if nb_old:
+            pre[s, nb_old - 1] = case.sibling_tables[s, nb_old - 1]
+    tables[:S] = pre
+    refs = np.zeros(NB, np.int64)
+    for row, n in zip(tables, ctx):
+        for b in row[: -(-int(n) // bs)]:
+            refs[b] += 1
+    free = np.flatnonzero(refs == 0).astype(np.int32)
+    stack = np.zeros(NB, np.int32)
+    stack[: len(free)] = free
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    d0 = [t(tables), t(ctx), t(refs), t(stack), t(np.array([len(free)]))]
+    seqs = t(np.arange(S))
+    slots = torch.empty(S, dtype=torch.int64, device=dev)
+    pairs = torch.empty((S, 2), dtype=torch.int64, device=dev)
+    npairs = torch.empty(1, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    nk, nv = W.to_torch(case.new_key, sp.dtype, dev), W.to_torch(case.new_value, sp.dtype, dev)
+    q = W.to_torch(case.query, sp.dtype, dev)
+    out = torch.empty_like(q)
+    maxb = tables.shape[1]
+    ws = torch.empty(max(256, ops.workspace_bytes(S, sp.num_heads, sp.num_kv_heads, sp.head_dim, bs,
+                                                  maxb, 0)), dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        d = [x.clone() for x in d0]          # every step starts from the same state
+        e = ev[i - warmup] if i >= warmup else None
+        if e:
+            e[0].record()
+        ops.append_slots(*d, seqs, bs, slots, pairs, npairs, status)
+        if e:
+            e[1].record()
+        ops.copy_blocks_counted(case.key_cache, case.value_cache, pairs, npairs, S)
+        if e:
+            e[2].record()
+        ops.reshape_and_cache(nk, nv, case.key_cache, case.value_cache, slots)
+        ops.decode(out, q, case.key_cache, case.value_cache, d[0][:S], d[1][:S],
+                   float(case.scale), shared_blocks=True, workspace=ws)
+        if e:
+            e[3].record()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device append failed with status {int(status.item())}")
+    med = lambda a, b: float(np.median([x[a].elapsed_time(x[b]) for x in ev]))
+    return {"append_slots_us": round(1e3 * med(0, 1), 2),
+            "copy_blocks_counted_us": round(1e3 * med(1, 2), 2),
+            "step_ms": round(med(0, 3), 4), "copy_pairs": int(npairs.item()),
+            "sequences": S}
+
+
 def run_workload(name, dev, steps, warmup, kernel):
     import torch
     case = W.build_case(W.CONFIGS[name], device=dev)
@@ -424,6 +492,8 @@ def main(argv=None):
         torch.cuda.empty_cache()
         for pname in ("prefill_llama7b", "prefill_gqa"):
             detail[pname] = measure_prefill(dev, pname, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        detail["shared_prefix_device_engine"] = measure_device_engine(dev, args.steps, args.warmup)
         rec["detail"] = detail
     if snaps is not None:
         rec["cpu_baseline"] = cpu_baseline(case, snaps, args.cpu_seconds)
