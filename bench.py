@@ -407,6 +407,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="time only these detail legs (comma-separated: a decode workload, "
+                         "prefill_llama7b, prefill_gqa, swap_blocks, device_engine) and print them")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -424,6 +427,27 @@ def main(argv=None):
     ops.load()
     if args.calibrate_copy:
         calibrate_copy(dev, args.steps)
+        return 0
+    if args.only:
+        res = {}
+        for leg in [x for x in args.only.split(",") if x]:
+            if leg in W.PREFILL_CONFIGS:
+                res[leg] = measure_prefill(dev, leg, args.steps, args.warmup)
+            elif leg == "swap_blocks":
+                res[leg] = measure_swap(dev, args.steps)
+            elif leg == "device_engine":
+                res[leg] = measure_device_engine(dev, args.steps, args.warmup)
+            elif leg in W.CONFIGS:
+                c2, st2, ms2, k2, _, _ = run_workload(leg, dev, args.steps, args.warmup, args.kernel)
+                res[leg] = {"ms_per_step": round(ms2, 4), "decode_kernel_ms": round(k2, 4),
+                            "decode_kernel_GBps": round(decode_bytes(c2) / (k2 * 1e-3) / 1e9, 2),
+                            "kernel": chosen_kernel(c2, args.kernel)}
+                del c2, st2
+            else:
+                print(f"unknown leg {leg!r}", file=sys.stderr)
+                return 2
+            torch.cuda.empty_cache()
+        print(json.dumps({"only": res}), flush=True)
         return 0
 
     name = args.workload
