@@ -177,8 +177,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
     }
   }
 
-  // Loader role: thread (tg, dc) moves tokens 4tg .. 4tg+3 of a tile, dims 8dc .. 8dc+7.
-  const int tg = tid >> 4, dc = tid & 15;
+  // Loader role: thread (tg, dc) moves tokens 4tg .. 4tg+3 of a tile, dims 8dc .. 8dc+7.  The
+  // 16 lanes of each LDS write phase are two token groups (tg, tg+4, whose V^T rows use the
+  // two 8-byte halves of a chunk) times 8 dim columns, so the transposed 8-byte writes land on
+  // 16 distinct bank pairs; 8 lanes still cover 128 contiguous bytes of a K/V row.
+  const int p16 = tid >> 4, l16 = tid & 15;
+  const int dc = (l16 & 7) | ((p16 & 1) << 3);
+  const int tg = ((p16 >> 1) & 3) | ((l16 >> 3) << 2) | ((p16 >> 3) << 3);
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int nb_live = (n + BS - 1) / BS;
   const size_t head_off = (size_t)kvh * BS * kRow;
