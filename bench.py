@@ -401,7 +401,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
-    ap.add_argument("--also", default="llama7b_bs32,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8",
+    ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -116,12 +116,13 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *                 decoded; must be <= max_blocks_per_seq * block_size (larger is clamped)
  *   scale         softmax scale (fp32), typically 1/sqrt(head_dim)
  *   partition_size  tokens per split-KV partition: 0 = library choice
- *                 (pa_decode_auto_partition), otherwise a positive multiple of block_size;
+ *                 (pa_decode_auto_partition), otherwise a positive multiple of block_size
+ *                 and of 16;
  *                 a partition size covering the whole table means a single pass
  *   workspace     device buffer of at least pa_decode_workspace_bytes(...) bytes (may be
  *                 NULL when that is 0); contents on entry are ignored
  *
- * Supported: block_size in {16, 32, 64, 128}; head_dim 64 or 128 for every 16/32-bit
+ * Supported: block_size in {8, 16, 32, 64, 128}; head_dim 64 or 128 for every 16/32-bit
  * pa_dtype, and also 80 or 256 for PA_F16 / PA_BF16; num_heads a multiple of num_kv_heads.  Slots past a sequence's context, unused blocks and unused
  * table entries are never read as values, so they may hold anything (NaN included).
  * Errors: PA_ERR_NULL_PTR, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
@@ -261,7 +262,7 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
  * Rows of a sequence with L_s > n, or n > max_blocks_per_seq * block_size, are written as
  * zeros; rows past max_query_len of a longer chunk are not written.  Only the first
  * ceil(n / block_size) table entries and the first n slots are read.
- * Supported: dtype f16 or bf16, head_dim 128, block_size 16, 32, 64 or 128.  Arithmetic: 16-bit
+ * Supported: dtype f16 or bf16, head_dim 128, block_size 8, 16, 32, 64 or 128.  Arithmetic: 16-bit
  * operands on the matrix cores with fp32 accumulation; the softmax probabilities keep about
  * 16 significant bits for bf16 (two products) and 11 for f16, unless flags has
  * PA_PREFILL_BF16_P, which rounds bf16 probabilities to bfloat16 once (one product, faster,
@@ -300,7 +301,7 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key
  * out are dtype (PA_F16 or PA_BF16); pools are uint8 as above; partition_size, workspace
  * (pa_decode_workspace_bytes with the same sizes), flags and errors as pa_decode_ex.
  * pa_decode_fp8_partitions is its first launch (pa_decode_merge, with the same dtype, is the
- * second).  Supported: head_dim 128, block_size 16, 32, 64 or 128.
+ * second).  Supported: head_dim 128, block_size 8, 16, 32, 64 or 128.
  */
 pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
                         const void* value_cache, const int32_t* block_tables,

@@ -50,8 +50,9 @@ pa_status check_shape(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
   if (S < 0 || Hq <= 0 || Hkv <= 0 || maxb <= 0 || partition_size < 0) return PA_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return PA_ERR_BAD_SHAPE;
   if (D != 64 && D != 80 && D != 128 && D != 256) return PA_ERR_UNSUPPORTED;
-  if (BS != 16 && BS != 32 && BS != 64 && BS != 128) return PA_ERR_UNSUPPORTED;
-  if (partition_size > 0 && partition_size % BS != 0) return PA_ERR_BAD_SHAPE;
+  if (BS != 8 && BS != 16 && BS != 32 && BS != 64 && BS != 128) return PA_ERR_UNSUPPORTED;
+  // partitions hold whole blocks and whole 16-token chunks
+  if (partition_size > 0 && partition_size % std::max<int32_t>(BS, 16) != 0) return PA_ERR_BAD_SHAPE;
   if ((long)maxb * BS > (1L << 30)) return PA_ERR_BAD_SHAPE;
   return PA_OK;
 }

@@ -6,7 +6,8 @@
 // matrix cores; the decode stays bound by HBM (about 4 flop per KV byte at G = 4), and the
 // matrix cores take the multiply-adds off the vector ALUs.
 //
-// Tiling.  A wave consumes one 16-token chunk (one block of 16, or half a block of 32) per step.
+// Tiling.  A wave consumes one 16-token chunk per step: a block of 16, a slice of a larger
+// block, or two blocks of 8 (then K loads 0-1 and lanes 0-31 of the V loads read the first).
 //   Scores: S^T[16 tokens x 16 cols] = K_chunk[16 x 128] * Q^T[128 x 16], four
 //     v_mfma_f32_16x16x32 ops.  Column n holds query head n mod GT (heads are replicated when
 //     GT < 16).  A operand (K): lane l holds K[token l%16][32kc + 8(l/16) .. +8]; B operand
@@ -68,7 +69,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   constexpr int D = 128;
   constexpr int EB = 2;            // element bytes
   constexpr int ROW = D * EB;      // 256-byte token row
-  constexpr int CPB = BS / 16;     // 16-token chunks per block
+  constexpr int CPB = BS >= 16 ? BS / 16 : 1;   // 16-token chunks per block
+  constexpr int BPC = BS >= 16 ? 1 : 16 / BS;   // blocks per chunk (2 for 8-token blocks)
+  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
   using M = Mfma<dt>;
   static_assert(GT == 4 || GT == 8 || GT == 16, "heads per workgroup");
 
@@ -99,11 +102,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     for (int kc = 0; kc < 4; ++kc)
       qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
   }
-  int ent_first = -1;
-  {
-    const int my_ch = ch_begin + wave + 4 * lane;
-    if (my_ch < p.max_blocks_per_seq * CPB) ent_first = table[my_ch / CPB];
-  }
+  // table entries of chunk ch: its block, or its two 8-token blocks (the second lies past the
+  // table row when the row length is odd)
+  auto fetch_entries = [&](int ch, int& e0, int& e1) {
+    if constexpr (BPC == 1) {
+      if (ch < p.max_blocks_per_seq * CPB) e0 = table[ch / CPB];
+    } else {
+      if (2 * ch < p.max_blocks_per_seq) e0 = table[2 * ch];
+      if (2 * ch + 1 < p.max_blocks_per_seq) e1 = table[2 * ch + 1];
+    }
+  };
+  int ent_first = -1, ent_first1 = -1;
+  fetch_entries(ch_begin + wave + 4 * lane, ent_first, ent_first1);
 
   int n = p.context_lens[s];
   n = min(n, p.max_blocks_per_seq * BS);
@@ -137,16 +147,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   __shared__ uint4 s_k[4][256];
   uint4* kst = s_k[wave];
 
-  auto load_chunk = [&](uint4 (&kb)[4], uint4 (&vb)[4], int phys, int ch) {
-    const size_t el = (size_t)phys * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
-    const char* kp = (const char*)p.kc + el * EB + lane * 16;
-    const char* vp = (const char*)p.vc + el * EB + v_off;
+  auto load_chunk = [&](uint4 (&kb)[4], uint4 (&vb)[4], int phys0, int phys1, int ch) {
+    const size_t el0 = (size_t)phys0 * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
+    if constexpr (BPC == 1) {
+      const char* kp = (const char*)p.kc + el0 * EB + lane * 16;
+      const char* vp = (const char*)p.vc + el0 * EB + v_off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kb[i] = load_kv<STREAM>(kp + 1024 * i);
+      for (int i = 0; i < 4; ++i) kb[i] = load_kv<STREAM>(kp + 1024 * i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vb[j] = load_kv<STREAM>(vp + j * ROW);
+      for (int j = 0; j < 4; ++j) vb[j] = load_kv<STREAM>(vp + j * ROW);
+    } else {
+      // tokens 0-7 in block phys0, 8-15 in phys1 (at offsets 0-7 there)
+      const size_t el1 = (size_t)phys1 * block_stride + head_off;
+      const char* kp0 = (const char*)p.kc + el0 * EB + lane * 16;
+      const char* kp1 = (const char*)p.kc + el1 * EB + lane * 16 - 2048;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kb[i] = load_kv<STREAM>((i < 2 ? kp0 : kp1) + 1024 * i);
+      const char* vp = (const char*)p.vc + (kg < 2 ? el0 : el1) * EB + v_off - (kg < 2 ? 0 : 8 * ROW);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vb[j] = load_kv<STREAM>(vp + j * ROW);
+    }
   };
-  auto consume = [&](const uint4 (&kb)[4], uint4 (&vb)[4], int ch, bool ok) {
+  // okm: bit b set when the chunk's block b has a valid id (both bits for blocks >= 16); this
+  // lane's tokens 4kg .. 4kg+3 lie in block kg/2 of an 8-token pair
+  auto consume = [&](const uint4 (&kb)[4], uint4 (&vb)[4], int ch, int okm) {
+    const bool ok = ((okm >> (BPC == 1 ? 0 : kg >> 1)) & 1) != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) kst[16 * (4 * i + kg) + (lr ^ (4 * i + kg))] = kb[i];
     uint4 kop[4];
@@ -156,7 +181,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) st = M::mma32(kop[kc], qb[kc], st);
     const int tok0 = ch * 16 + 4 * kg;   // token of register j is tok0 + j
-    const bool full = ok && (ch * 16 + 16 <= t_end);
+    const bool full = okm == 3 && (ch * 16 + 16 <= t_end);
     float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = st[j] * p.scale_log2;
@@ -206,29 +231,44 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   // lane, and broadcast with readlane (the first 64 were fetched above)
   for (int base = ch_begin + wave; base < ch_end; base += 4 * kWave) {
     const int cnt = min(kWave, (ch_end - base + 3) / 4);
-    int ent = ent_first;
+    int ent = ent_first, ent1 = ent_first1;
     if (base != ch_begin + wave) {
-      const int my_ch = base + 4 * lane;
-      ent = lane < cnt ? table[my_ch / CPB] : -1;
+      ent = ent1 = -1;
+      if (lane < cnt) fetch_entries(base + 4 * lane, ent, ent1);
     }
-    auto phys_of = [&](int i, bool& ok) {
-      const int b = __builtin_amdgcn_readlane(ent, i);
-      ok = (unsigned)b < (unsigned)p.num_blocks;   // a bad id reads block 0 and is masked
-      return ok ? b : 0;
+    // ids of chunk i's block(s); a bad id reads block 0 and its tokens are masked
+    int ph0, ph1;
+    auto phys_of = [&](int i, int& okm) {
+      const int b0 = __builtin_amdgcn_readlane(ent, i);
+      const bool ok0 = (unsigned)b0 < (unsigned)p.num_blocks;
+      ph0 = ok0 ? b0 : 0;
+      if constexpr (BPC == 1) {
+        okm = ok0 ? 3 : 0;
+        ph1 = ph0;
+      } else {
+        const int b1 = __builtin_amdgcn_readlane(ent1, i);
+        const bool ok1 = (unsigned)b1 < (unsigned)p.num_blocks;
+        ph1 = ok1 ? b1 : 0;
+        okm = (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
+      }
     };
     // Two register buffers, steady-state loads unconditional (see the vector-ALU kernel).
     uint4 ka[4], va[4], kb[4], vb[4];
-    bool oka, okb;
-    load_chunk(ka, va, phys_of(0, oka), base);
+    int oka, okb;
+    phys_of(0, oka);
+    load_chunk(ka, va, ph0, ph1, base);
     int i = 0;
     for (; i + 2 < cnt; i += 2) {
-      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      phys_of(i + 1, okb);
+      load_chunk(kb, vb, ph0, ph1, base + 4 * (i + 1));
       consume(ka, va, base + 4 * i, oka);
-      load_chunk(ka, va, phys_of(i + 2, oka), base + 4 * (i + 2));
+      phys_of(i + 2, oka);
+      load_chunk(ka, va, ph0, ph1, base + 4 * (i + 2));
       consume(kb, vb, base + 4 * (i + 1), okb);
     }
     if (i + 1 < cnt) {
-      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      phys_of(i + 1, okb);
+      load_chunk(kb, vb, ph0, ph1, base + 4 * (i + 1));
       consume(ka, va, base + 4 * i, oka);
       consume(kb, vb, base + 4 * (i + 1), okb);
     } else {
@@ -297,6 +337,7 @@ hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
 
 template <DT dt>
 hipError_t launch_bs(int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
+  if (bs == 8) return sk ? launch_gt<dt, 8, true>(gt, p, grid, st) : launch_gt<dt, 8, false>(gt, p, grid, st);
   if (bs == 16) return sk ? launch_gt<dt, 16, true>(gt, p, grid, st) : launch_gt<dt, 16, false>(gt, p, grid, st);
   if (bs == 32) return sk ? launch_gt<dt, 32, true>(gt, p, grid, st) : launch_gt<dt, 32, false>(gt, p, grid, st);
   if (bs == 64) return sk ? launch_gt<dt, 64, true>(gt, p, grid, st) : launch_gt<dt, 64, false>(gt, p, grid, st);

@@ -40,10 +40,12 @@ struct ValuCfg {
   static constexpr int LPT = VC <= 8 ? 8 : VC <= 16 ? 16 : 32;
   static constexpr int TPI = kWave / LPT;    // tokens per wave load instruction
   static constexpr int NI = 16 / TPI;        // load instructions per 16-token chunk
-  static constexpr int CPB = BS / 16;        // chunks per block
+  static constexpr int CPB = BS >= 16 ? BS / 16 : 1;   // chunks per block
+  static constexpr int BPC = BS >= 16 ? 1 : 16 / BS;   // blocks per chunk (2 for 8-token blocks)
   static constexpr int ROW_BYTES = D * E::kBytes;
   static_assert(VC * EPL == D && VC >= 4 && VC <= 32, "row must be 4..32 whole vectors");
-  static_assert(BS % 16 == 0, "block size must be a multiple of 16");
+  static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
+  static_assert(TPI <= BS, "one load instruction must stay inside one block");
 };
 
 template <DT dt, DT kt, int D, int BS, int GT, bool STREAM>
@@ -52,6 +54,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   using E = typename C::E;
   using Q = typename C::Q;
   constexpr int EPL = C::EPL, LPT = C::LPT, TPI = C::TPI, NI = C::NI, CPB = C::CPB, QV = C::QV;
+  constexpr int BPC = C::BPC;
   constexpr int VC = C::VC;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -85,11 +88,18 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     for (int v = 0; v < QV; ++v)
       qraw[h][v] = *reinterpret_cast<const uint4*>(
           (const char*)p.q + (q_row0 + (size_t)h * D + colc * EPL) * Q::kBytes + 16 * v);
-  int ent_first = -1;
-  {
-    const int my_ch = ch_begin + wave + 4 * lane;
-    if (my_ch < p.max_blocks_per_seq * CPB) ent_first = table[my_ch / CPB];
-  }
+  // table entries of chunk ch: its block (blocks of >= 16 tokens), or its two blocks e0, e1
+  // (8-token blocks; the second lies past the table row when the row length is odd)
+  auto fetch_entries = [&](int ch, int& e0, int& e1) {
+    if constexpr (BPC == 1) {
+      if (ch < p.max_blocks_per_seq * CPB) e0 = table[ch / CPB];
+    } else {
+      if (2 * ch < p.max_blocks_per_seq) e0 = table[2 * ch];
+      if (2 * ch + 1 < p.max_blocks_per_seq) e1 = table[2 * ch + 1];
+    }
+  };
+  int ent_first = -1, ent_first1 = -1;
+  fetch_entries(ch_begin + wave + 4 * lane, ent_first, ent_first1);
 
   int n = p.context_lens[s];
   n = min(n, p.max_blocks_per_seq * BS);
@@ -138,22 +148,34 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
   const int lane_off = (row * D + colc * EPL) * E::kBytes;   // bytes inside a 16-token chunk
 
-  // address of this lane's first vector of chunk `ch` (physical block `phys`)
+  // address of this lane's first vector of chunk `ch` (physical block `phys`); with 8-token
+  // blocks, of the chunk's half in block `phys`
   auto chunk_ptr = [&](const void* base, int phys, int ch) -> const char* {
     const size_t el = (size_t)phys * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
     return (const char*)base + el * E::kBytes + lane_off;
   };
-  auto load_chunk = [&](uint4 (&kb)[NI], uint4 (&vb)[NI], int phys, int ch) {
-    const char* kp = chunk_ptr(p.kc, phys, ch);
-    const char* vp = chunk_ptr(p.vc, phys, ch);
+  // load i covers chunk tokens i*TPI + row, inside the chunk's block i*TPI*BPC/16
+  auto load_chunk = [&](uint4 (&kb)[NI], uint4 (&vb)[NI], int phys0, int phys1, int ch) {
+    const char* kp0 = chunk_ptr(p.kc, phys0, ch);
+    const char* vp0 = chunk_ptr(p.vc, phys0, ch);
+    const char* kp1 = BPC == 1 ? kp0 : chunk_ptr(p.kc, phys1, ch);
+    const char* vp1 = BPC == 1 ? vp0 : chunk_ptr(p.vc, phys1, ch);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kb[i] = load_kv<STREAM>(kp + i * TPI * C::ROW_BYTES);
+    for (int i = 0; i < NI; ++i) {
+      const int t = i * TPI, hb = BPC == 1 ? 0 : t / BS;
+      kb[i] = load_kv<STREAM>((hb ? kp1 : kp0) + (t - hb * BS) * C::ROW_BYTES);
+    }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vb[i] = load_kv<STREAM>(vp + i * TPI * C::ROW_BYTES);
+    for (int i = 0; i < NI; ++i) {
+      const int t = i * TPI, hb = BPC == 1 ? 0 : t / BS;
+      vb[i] = load_kv<STREAM>((hb ? vp1 : vp0) + (t - hb * BS) * C::ROW_BYTES);
+    }
   };
-  auto consume = [&](const uint4 (&kb)[NI], const uint4 (&vb)[NI], int ch, bool ok) {
+  // okm: bit b set when the chunk's block b has a valid id (both bits for blocks >= 16)
+  auto consume = [&](const uint4 (&kb)[NI], const uint4 (&vb)[NI], int ch, int okm) {
     const int tok0 = ch * 16 + row;
-    const bool full = ok && (ch * 16 + 16 <= t_end);
+    const bool full = okm == 3 && (ch * 16 + 16 <= t_end);
+    auto ok_of = [&](int i) { return ((okm >> (BPC == 1 ? 0 : i * TPI / BS)) & 1) != 0; };
     float sc[NI][GT];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -167,7 +189,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
         sc[i][h] = group_sum<LPT>(acc);
       }
       if (!full) {
-        const bool valid = ok && (tok0 + i * TPI < t_end);
+        const bool valid = ok_of(i) && (tok0 + i * TPI < t_end);
 #pragma unroll
         for (int h = 0; h < GT; ++h) sc[i][h] = valid ? sc[i][h] : -INFINITY;
       }
@@ -197,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       float vf[EPL];
       E::unpack(vb[i], vf);
       if (!full) {
-        const bool valid = ok && (tok0 + i * TPI < t_end);
+        const bool valid = ok_of(i) && (tok0 + i * TPI < t_end);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vf[e] = valid ? vf[e] : 0.0f;  // masked slots may hold NaN
       }
@@ -212,31 +234,46 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   // one per lane, and broadcast with readlane (the first 64 were fetched above)
   for (int base = ch_begin + wave; base < ch_end; base += 4 * kWave) {
     const int cnt = min(kWave, (ch_end - base + 3) / 4);
-    int ent = ent_first;
+    int ent = ent_first, ent1 = ent_first1;
     if (base != ch_begin + wave) {
-      const int my_ch = base + 4 * lane;
-      ent = lane < cnt ? table[my_ch / CPB] : -1;
+      ent = ent1 = -1;
+      if (lane < cnt) fetch_entries(base + 4 * lane, ent, ent1);
     }
-    auto phys_of = [&](int i, bool& ok) {
-      int b = __builtin_amdgcn_readlane(ent, i);
-      ok = (unsigned)b < (unsigned)p.num_blocks;   // a bad id reads block 0 and is masked
-      return ok ? b : 0;
+    // ids of chunk i's block(s); a bad id reads block 0 and its tokens are masked
+    int ph0, ph1;
+    auto phys_of = [&](int i, int& okm) {
+      const int b0 = __builtin_amdgcn_readlane(ent, i);
+      const bool ok0 = (unsigned)b0 < (unsigned)p.num_blocks;
+      ph0 = ok0 ? b0 : 0;
+      if constexpr (BPC == 1) {
+        okm = ok0 ? 3 : 0;
+        ph1 = ph0;
+      } else {
+        const int b1 = __builtin_amdgcn_readlane(ent1, i);
+        const bool ok1 = (unsigned)b1 < (unsigned)p.num_blocks;
+        ph1 = ok1 ? b1 : 0;
+        okm = (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
+      }
     };
     // Two register buffers; in the steady state every iteration issues the next chunk's
     // loads unconditionally before consuming the current one, so the wait before a consume
     // covers only the older chunk (a conditional load would force a wait for everything).
     uint4 ka[NI], va[NI], kb[NI], vb[NI];
-    bool oka, okb;
-    load_chunk(ka, va, phys_of(0, oka), base);
+    int oka, okb;
+    phys_of(0, oka);
+    load_chunk(ka, va, ph0, ph1, base);
     int i = 0;
     for (; i + 2 < cnt; i += 2) {
-      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      phys_of(i + 1, okb);
+      load_chunk(kb, vb, ph0, ph1, base + 4 * (i + 1));
       consume(ka, va, base + 4 * i, oka);
-      load_chunk(ka, va, phys_of(i + 2, oka), base + 4 * (i + 2));
+      phys_of(i + 2, oka);
+      load_chunk(ka, va, ph0, ph1, base + 4 * (i + 2));
       consume(kb, vb, base + 4 * (i + 1), okb);
     }
     if (i + 1 < cnt) {
-      load_chunk(kb, vb, phys_of(i + 1, okb), base + 4 * (i + 1));
+      phys_of(i + 1, okb);
+      load_chunk(kb, vb, ph0, ph1, base + 4 * (i + 1));
       consume(ka, va, base + 4 * i, oka);
       consume(kb, vb, base + 4 * (i + 1), okb);
     } else {
@@ -352,6 +389,7 @@ hipError_t launch_bs(int bs, int gt, bool stream_kv, const DecodeParams& p, int 
                      : launch_gt<dt, kt, D, BS, false>(gt, p, grid, st);
   };
   switch (bs) {
+    case 8: return go(std::integral_constant<int, 8>{});
     case 16: return go(std::integral_constant<int, 16>{});
     case 32: return go(std::integral_constant<int, 32>{});
     case 64: return go(std::integral_constant<int, 64>{});

@@ -99,7 +99,7 @@ __device__ __forceinline__ float row_max4(float x) {
 template <DT dt, int BS, bool SPLIT_P>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParams p) {
   using M = Mma<dt>;
-  static_assert(BS % 16 == 0, "a thread's 4 tokens must sit in one block");
+  static_assert(BS % 8 == 0, "a thread's 4 tokens must sit in one block");
   __shared__ uint4 s_k[2][kTile * 16];
   __shared__ uint4 s_v[2][kD * 8];
 
@@ -404,6 +404,7 @@ hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const Prefil
     constexpr DT T = decltype(dt_tag)::value;
     constexpr bool SP = decltype(split_tag)::value;
     switch (block_size) {
+      case 8: return go<T, 8, SP>(p, grid, st);
       case 16: return go<T, 16, SP>(p, grid, st);
       case 32: return go<T, 32, SP>(p, grid, st);
       case 64: return go<T, 64, SP>(p, grid, st);

@@ -120,6 +120,8 @@ CONFIGS = {
                              ("lognormal", 700.0, 1.0, 16, 4096)),
     "llama7b_bs32": CaseSpec("llama7b_bs32", 3, 256, 32, 32, 128, "bf16", 32,
                              ("lognormal", 700.0, 1.0, 16, 4096)),
+    "llama7b_bs8": CaseSpec("llama7b_bs8", 3, 256, 32, 32, 128, "bf16", 8,
+                            ("lognormal", 700.0, 1.0, 16, 4096)),
     "gqa_long": CaseSpec("gqa_long", 4, 16, 32, 8, 128, "bf16", 16, ("uniform", 8192, 32768),
                          partition_size=512),
     "shared_prefix": CaseSpec("shared_prefix", 5, 64, 32, 32, 128, "f16", 16,

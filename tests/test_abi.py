@@ -58,7 +58,11 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, P=24) == 2                   # not a multiple of block_size
     assert _decode(lib, scale=float("nan")) == 2
     assert _decode(lib, D=96) == 3                   # PA_ERR_UNSUPPORTED
-    assert _decode(lib, BS=8) == 3
+    assert _decode(lib, BS=4) == 3
+    assert _decode(lib, BS=48) == 3
+    assert _decode(lib, BS=8, out=0) == 1             # 8-token blocks accepted
+    assert _decode(lib, BS=8, P=24) == 2              # partitions hold whole 16-token chunks
+    assert _decode(lib, BS=8, P=32, out=0) == 1
     assert _decode(lib, D=80, dtype=0) == 3          # fp32 rows: head_dim 64 or 128 only
     assert _decode(lib, D=256, BS=128, out=0) == 1   # 256 dims and 128-token blocks accepted
     assert _decode(lib, dtype=7) == 3
@@ -137,7 +141,8 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, scale=float("inf")) == 2
     assert _prefill(lib, dtype=0) == 3               # PA_ERR_UNSUPPORTED: f32
     assert _prefill(lib, D=64) == 3
-    assert _prefill(lib, BS=8) == 3
+    assert _prefill(lib, BS=4) == 3
+    assert _prefill(lib, BS=8, out=0) == 1            # 8-token blocks accepted
     assert _prefill(lib, flags=0x2) == 3
     assert _prefill(lib, flags=0x1, out=0) == 1      # the bf16-probabilities flag is accepted
     assert _prefill(lib, S=0, out=0) == 0            # nothing to do

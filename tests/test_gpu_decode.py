@@ -32,14 +32,14 @@ def _mfma_ok(dtype, D, Hq, Hkv, P):
 
 @pytest.mark.parametrize("partition", [0, 64, 48])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("BS", [8, 16, 32])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_decode_matches_oracle(dtype, D, BS, kernel, partition):
     dev = need_gpu()
     Hq, Hkv = 8, 2
-    if partition % BS:
-        pytest.skip("partition must be a multiple of the block size")
+    if partition % max(BS, 16):
+        pytest.skip("partition must be a multiple of the block size and of 16")
     if kernel == "mfma" and not _mfma_ok(dtype, D, Hq, Hkv, partition or 512):
         pytest.skip("matrix-core kernel needs f16/bf16, head_dim 128, groups of 4k")
     say(f"decode {dtype} D={D} BS={BS} kernel={kernel} P={partition}")
@@ -68,8 +68,30 @@ def test_large_blocks(dtype, kernel, BS):
                                f"BS{BS}/{kernel}/P{P}")
 
 
+@pytest.mark.parametrize("fill", [-1, 2**31 - 1])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_block_size_8_table_edges(kernel, fill):
+    """8-token blocks: a 16-token chunk spans two blocks.  An odd table width whose last row
+    entry is in use (the chunk's second block lies past the row), chunks whose second block is
+    past the context (junk entry, NaN slots), partitions of one chunk; same bits as the clean
+    run and within the oracle bar."""
+    dev = need_gpu()
+    lengths = [1, 7, 8, 9, 15, 16, 17, 104, 99]
+    spec = W.CaseSpec("bs8", 18, len(lengths), 8, 2, 128, "bf16", 8, ("fixed", lengths),
+                      new_tokens=("free", 0), max_blocks_per_seq=13)
+    clean = W.build_case(spec)
+    dirty = W.build_case(spec, poison=True, table_fill=fill)
+    ref = oracle_decode(clean)
+    for P in (0, 16, 48):
+        a = Uploaded(clean, dev).decode(kernel, P)
+        b = Uploaded(dirty, dev).decode(kernel, P)
+        assert np.all(np.isfinite(oracle.storage_to_f64(b, "bf16")))
+        assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
+        assert_attention_close(a, ref, "bf16", live_vmax(clean), f"bs8/{kernel}/P{P}")
+
+
 @pytest.mark.parametrize("heads", [(8, 8), (8, 2), (4, 1)])
-@pytest.mark.parametrize("BS", [16, 64])
+@pytest.mark.parametrize("BS", [8, 16, 64])
 @pytest.mark.parametrize("D", [80, 256])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_head_dims_80_256(dtype, D, BS, heads):

@@ -62,6 +62,7 @@ MATRIX = [
     ("bf16", 16, 4, 1, (2048, 1500), 256),            # G = 4, many partitions
     ("bf16", 64, 8, 8, (1, 63, 64, 65, 700), 128),    # 64-token blocks
     ("f16", 128, 4, 2, (1, 127, 129, 900), 0),        # 128-token blocks
+    ("bf16", 8, 8, 2, (1, 7, 8, 9, 300), 16),         # 8-token blocks, one-chunk partitions
 ]
 
 

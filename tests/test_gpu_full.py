@@ -62,7 +62,8 @@ def _oracle_seq(case, s, snap):
     return out[0], kc, vc, float(np.max(np.abs(V)))
 
 
-@pytest.mark.parametrize("name", ["opt13b", "llama7b_bs16", "llama7b_bs32", "gqa_long", "shared_prefix"])
+@pytest.mark.parametrize("name", ["opt13b", "llama7b_bs16", "llama7b_bs32", "llama7b_bs8", "gqa_long",
+                                  "shared_prefix"])
 def test_full_size_sampled(name):
     import torch
     dev = need_gpu()

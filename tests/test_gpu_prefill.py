@@ -85,6 +85,7 @@ MATRIX = [
     ("bf16", 32, 2, 1, (0, 0), (300, 257)),                    # whole prompts, many tiles
     ("bf16", 64, 4, 4, (0, 100, 63), (70, 129, 1)),             # 64-token blocks
     ("f16", 128, 8, 2, (5, 300), (200, 1)),                     # 128-token blocks
+    ("bf16", 8, 8, 2, (0, 7, 8, 101), (9, 1, 64, 70)),          # 8-token blocks
 ]
 
 
