@@ -120,7 +120,8 @@ def pin_sdpa_library(O):
     """Paged oracle == torch's float64 SDPA on the contiguous logical K/V (GQA head mapping
     taken from torch's convention), over block sizes, head dims and element types."""
     combos = [("f32", 16, 64, 2, 2), ("f16", 16, 128, 4, 1), ("bf16", 32, 128, 8, 2),
-              ("bf16", 16, 64, 4, 4), ("f32", 32, 16, 6, 3)]
+              ("bf16", 16, 64, 4, 4), ("f32", 32, 16, 6, 3), ("f16", 8, 32, 4, 2),
+              ("bf16", 64, 16, 2, 1)]
     for i, (dtype, bs, d, Hq, Hkv) in enumerate(combos):
         c = _case(S=4, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, bs=bs, lengths=(1, bs - 1, bs + 1, 3 * bs + 7),
                   seed=20 + i)
