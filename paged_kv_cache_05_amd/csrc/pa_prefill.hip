@@ -248,121 +248,136 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   stash(0);
   __syncthreads();
 
+  // The steps of one 32-token half h of the tile in LDS buffer `buf`:
+  //   scores:  S^T = K Q^T (16 MFMAs)
+  //   mask:    causal mask, only where the half reaches past some row's last position (a
+  //            branch holding a scheduling barrier, so fully visible halves pay nothing)
+  //   core:    row max (raw scores: scale > 0 commutes with max), lazy running max,
+  //            probabilities exp2(s * scale_log2 - m) with one FMA each, packed as B operand
+  //   rescale: O and l times alpha, only when some row's reference point moved (a branch)
+  //   accumulate: l += ones^T P^T and O^T += V^T P^T on the matrix cores
+  // Halves are software-pipelined inside the wave: the second half's score MFMAs sit in the
+  // same basic block as the first half's softmax, and the first half's output MFMAs in the
+  // same block as the second half's softmax, so the compiler's scheduler can let one wave keep
+  // its matrix core and its vector ALU busy at once (the two halves are independent there;
+  // the branches -- masking, rescale -- sit between those blocks).  Forcing a fixed
+  // MFMA / VALU interleave with scheduling-group barriers measured much slower.
+  using St = f32x4[2][2];   // [16-token block][row block]
+  auto scores = [&](St& st, int buf, int h) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int j = 2 * h + jb;
+      st[jb][0] = st[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 a = s_k[buf][(16 * j + lr) * 16 + ((4 * c + lg) ^ lr)];
+        st[jb][0] = M::mma(a, qb[0][c], st[jb][0]);
+        st[jb][1] = M::mma(a, qb[1][c], st[jb][1]);
+      }
+    }
+  };
+  auto mask = [&](St& st, int tstart) {
+    if (tstart + 31 > w_kv_min) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tstart + 16 * jb + 4 * lg + i > lim[c2]) st[jb][c2][i] = -INFINITY;
+    }
+  };
+  // Lazy running max (log2 units): the reference point moves only when a row's max exceeds
+  // it by more than kLazy, so probabilities stay below 2^kLazy and the O/l rescale runs only on
+  // the few steps where some row's max jumps.  Any reference point gives the same o / l;
+  // position 0, in every row's first half, makes the first step always move it from -inf.
+  // Returns whether any row of the wave moved (alpha[c2] = its factor, 1 for the others).
+  auto core = [&](St& st, uint4 (&ph)[2], uint4 (&pl)[2], float (&alpha)[2]) -> bool {
+    bool any_grow = false;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[jb][c2][i]);
+      mx = row_max4(mx);
+      const float ms = mx == -INFINITY ? -INFINITY : mx * p.scale_log2;
+      const bool grow = ms > m_run[c2] + kLazy;
+      const float m_new = grow ? ms : m_run[c2];
+      alpha[c2] = grow ? fast_exp2(m_run[c2] - m_new) : 1.0f;
+      m_run[c2] = m_new;
+      any_grow |= grow;
+      const float neg_m = -m_new;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(st[e >> 2][c2][e & 3], p.scale_log2, neg_m));
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        hw[e >> 1] = M::pack2(pv[e], pv[e + 1]);
+        if constexpr (SPLIT_P) {
+          const float r0 = pv[e] - __uint_as_float(hw[e >> 1] << 16);
+          const float r1 = pv[e + 1] - __uint_as_float(hw[e >> 1] & 0xFFFF0000u);
+          lw[e >> 1] = M::pack2(r0, r1);
+        }
+      }
+      ph[c2] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if constexpr (SPLIT_P) pl[c2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    return __any(any_grow);
+  };
+  auto rescale = [&](const float (&alpha)[2]) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      l_acc[c2] *= alpha[c2];
+#pragma unroll
+      for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][c2] *= alpha[c2];
+    }
+  };
+  auto accumulate = [&](const uint4 (&ph)[2], const uint4 (&pl)[2], int buf, int h) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      l_acc[c2] = M::mma(ones, ph[c2], l_acc[c2]);
+      if constexpr (SPLIT_P) l_acc[c2] = M::mma(ones, pl[c2], l_acc[c2]);
+    }
+#pragma unroll
+    for (int dt2 = 0; dt2 < 8; ++dt2) {
+      const int d = 16 * dt2 + lr;
+      const uint4 a = s_v[buf][d * 8 + ((4 * h + lg) ^ vswz(d))];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, ph[c2], o[dt2][c2]);
+      if constexpr (SPLIT_P) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, pl[c2], o[dt2][c2]);
+      }
+    }
+  };
+
   for (int k = 0; k < ntiles; ++k) {
     const int buf = k & 1;
     const bool more = k + 1 < ntiles;
     const int ent_after = entry(k + 2);
     if (more) issue(k + 1, ent_next);
 
-    // The tile is consumed in two 32-token halves, each a complete online-softmax step
-    // (scores, max, rescale, probabilities, products).  Both halves' scores are issued first,
-    // so the matrix cores work on the second half's scores while the vector ALUs run the
-    // first half's softmax.
-    f32x4 sts[2][2][2];   // [half][16-token block][row block]
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (!(wave_active && k * kTile + 32 * h < w_kv_end)) continue;   // wave-uniform
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const int j = 2 * h + jb;
-        sts[h][jb][0] = sts[h][jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 a = s_k[buf][(16 * j + lr) * 16 + ((4 * c + lg) ^ lr)];
-          sts[h][jb][0] = M::mma(a, qb[0][c], sts[h][jb][0]);
-          sts[h][jb][1] = M::mma(a, qb[1][c], sts[h][jb][1]);
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int tstart = k * kTile + 32 * h;
-      if (!(wave_active && tstart < w_kv_end)) continue;   // wave-uniform
-      f32x4 (&st)[2][2] = sts[h];
-      // Causal mask (only where the half reaches past some row's last position) and the row
-      // max, both on the raw scores: scale > 0, so the max commutes with it.  The masking
-      // branch holds a scheduling barrier so that it stays a branch (halves every row sees
-      // in full then carry no per-score compare).
-      if (tstart + 31 > w_kv_min) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (tstart + 16 * jb + 4 * lg + i > lim[c2]) st[jb][c2][i] = -INFINITY;
-      }
-      float mx[2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        mx[c2] = -INFINITY;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx[c2] = fmaxf(mx[c2], st[jb][c2][i]);
-        mx[c2] = row_max4(mx[c2]);
-      }
-      // Lazy running max (log2 units): the reference point moves only when a row's max
-      // exceeds it by more than kLazy, so probabilities stay below 2^kLazy and the O/l rescale
-      // (64 multiplies per lane) runs only on the few steps where some row's max jumps.  Any
-      // reference point gives the same o / l; position 0, in every row's first half, makes
-      // the first step always move it from -inf.
-      bool grow[2];
-      float m_new[2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const float ms = mx[c2] == -INFINITY ? -INFINITY : mx[c2] * p.scale_log2;
-        grow[c2] = ms > m_run[c2] + kLazy;
-        m_new[c2] = grow[c2] ? ms : m_run[c2];
-      }
-      if (__any(grow[0] || grow[1])) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const float alpha = grow[c2] ? fast_exp2(m_run[c2] - m_new[c2]) : 1.0f;
-          m_run[c2] = m_new[c2];
-          l_acc[c2] *= alpha;
-#pragma unroll
-          for (int dt2 = 0; dt2 < 8; ++dt2) o[dt2][c2] *= alpha;
-        }
-      }
-      // Probabilities exp2(s * scale_log2 - m) with one FMA each, packed as the B operand.
-      uint4 ph[2], pl[2];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const float neg_m = -m_run[c2];
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pv[e] = fast_exp2(fmaf(st[e >> 2][c2][e & 3], p.scale_log2, neg_m));
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          hw[e >> 1] = M::pack2(pv[e], pv[e + 1]);
-          if constexpr (SPLIT_P) {
-            const float r0 = pv[e] - __uint_as_float(hw[e >> 1] << 16);
-            const float r1 = pv[e + 1] - __uint_as_float(hw[e >> 1] & 0xFFFF0000u);
-            lw[e >> 1] = M::pack2(r0, r1);
-          }
-        }
-        ph[c2] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        l_acc[c2] = M::mma(ones, ph[c2], l_acc[c2]);
-        if constexpr (SPLIT_P) {
-          pl[c2] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-          l_acc[c2] = M::mma(ones, pl[c2], l_acc[c2]);
-        }
-      }
-#pragma unroll
-      for (int dt2 = 0; dt2 < 8; ++dt2) {
-        const int d = 16 * dt2 + lr;
-        const uint4 a = s_v[buf][d * 8 + ((4 * h + lg) ^ vswz(d))];
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, ph[c2], o[dt2][c2]);
-        if constexpr (SPLIT_P) {
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, pl[c2], o[dt2][c2]);
-        }
-      }
+    const int t0 = k * kTile;
+    // A wave whose rows all end before this tile skips it; a second half past all of its rows
+    // is masked whole (zero probabilities), which costs one idle half per wave at most.
+    St st0, st1;
+    uint4 ph0[2], pl0[2], ph1[2], pl1[2];
+    float al0[2], al1[2];
+    if (wave_active && t0 < w_kv_end) {   // wave-uniform
+      scores(st0, buf, 0);
+      mask(st0, t0);
+      scores(st1, buf, 1);
+      const bool g0 = core(st0, ph0, pl0, al0);
+      mask(st1, t0 + 32);
+      if (g0) rescale(al0);
+      accumulate(ph0, pl0, buf, 0);
+      const bool g1 = core(st1, ph1, pl1, al1);
+      if (g1) rescale(al1);
+      accumulate(ph1, pl1, buf, 1);
     }
 
     if (more) stash(buf ^ 1);
