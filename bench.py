@@ -65,6 +65,22 @@ def decode_bytes(case) -> int:
     return kv + qo + tables
 
 
+def decode_unique_kv_bytes(case) -> int:
+    """K/V bytes of the distinct (physical block, slot) rows one decode call reads: a block
+    that several sequences share (a common prefix) counts once.  Equal to the K/V part of
+    decode_bytes when nothing is shared."""
+    sp = case.spec
+    bs = sp.block_size
+    ekv = W.ELEM_BYTES[sp.kv_dtype or sp.dtype]
+    rows = {}
+    for s in range(sp.num_seqs):
+        n = int(case.context_lens[s])
+        for j in range(-(-n // bs)):
+            b = int(case.block_tables[s, j])
+            rows[b] = max(rows.get(b, 0), min(bs, n - j * bs))
+    return sum(rows.values()) * sp.num_kv_heads * sp.head_dim * ekv * 2
+
+
 def cache_write_bytes(case) -> int:
     sp = case.spec
     e = W.ELEM_BYTES[sp.dtype]
@@ -401,7 +417,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
-    ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8",
+    ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8,tiny",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -441,7 +457,12 @@ def main(argv=None):
                 c2, st2, ms2, k2, _, _ = run_workload(leg, dev, args.steps, args.warmup, args.kernel)
                 res[leg] = {"ms_per_step": round(ms2, 4), "decode_kernel_ms": round(k2, 4),
                             "decode_kernel_GBps": round(decode_bytes(c2) / (k2 * 1e-3) / 1e9, 2),
+                            "seq_heads_per_s": round(c2.spec.num_seqs * c2.spec.num_heads / (ms2 * 1e-3), 1),
                             "kernel": chosen_kernel(c2, args.kernel)}
+                if c2.spec.shared_prefix:
+                    ub = decode_unique_kv_bytes(c2)
+                    res[leg]["unique_kv_bytes"] = ub
+                    res[leg]["decode_kernel_unique_GBps"] = round(ub / (k2 * 1e-3) / 1e9, 2)
                 del c2, st2
             else:
                 print(f"unknown leg {leg!r}", file=sys.stderr)
@@ -508,6 +529,10 @@ def main(argv=None):
                          "decode_kernel_GBps": round(b2 / (k2 * 1e-3) / 1e9, 2),
                          "seq_heads_per_s": round(c2.spec.num_seqs * c2.spec.num_heads / (ms2 * 1e-3), 1),
                          "kernel": chosen_kernel(c2, args.kernel)}
+        if c2.spec.shared_prefix:
+            ub = decode_unique_kv_bytes(c2)
+            detail[extra]["unique_kv_bytes"] = ub
+            detail[extra]["decode_kernel_unique_GBps"] = round(ub / (k2 * 1e-3) / 1e9, 2)
         del c2
     if detail:
         del step
