@@ -218,3 +218,18 @@ def test_shared_blocks_flag_changes_nothing(kernel):
         b = u.decode(kernel, P, shared_blocks=True)
         assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
         assert_attention_close(b, oracle_decode(c), "bf16", live_vmax(c), f"shared-flag/{kernel}/P{P}")
+
+
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_very_long_context(kernel):
+    """128K-token and odd-length long contexts next to a short one: hundreds of partitions per
+    sequence at 512 tokens (every merge lane walks several partials), and the library's own
+    partition choice."""
+    dev = need_gpu()
+    lengths = [131072, 70001, 5]
+    say(f"decode {kernel} very long contexts {lengths}")
+    c = _case("bf16", 128, 16, 8, 2, lengths=lengths, seed=19)
+    u = Uploaded(c, dev)
+    ref = oracle_decode(c)
+    for P in (512, 0):
+        assert_attention_close(u.decode(kernel, P), ref, "bf16", live_vmax(c), f"long/{kernel}/P{P}")

@@ -211,3 +211,27 @@ def test_prefill_full_size_sampled():
                                      np.array([0, 1], np.int32),
                                      np.array([n - L + i + 1], np.int32), bs, case.scale, "bf16")
             assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
+
+
+def test_prefill_long_chunks_sampled():
+    """Long chunks (4096 tokens on a 4000-token prefix, and a 3000-token prompt) with G = 4:
+    128 row tiles per (sequence, KV head); sampled rows against the oracle on one-row chunks,
+    including each chunk's first and last row."""
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec("bf16", 16, 8, 2, (4000, 0), (4096, 3000), seed=14))
+    say("prefill long chunks (4096 on 4000 cached, 3000)")
+    got = Prefill(case, dev).run()
+    assert np.all(np.isfinite(oracle.storage_to_f64(got, "bf16")))
+    rng = np.random.default_rng(15)
+    vmax = vmax_of(case)
+    for s in range(2):
+        n, L = int(case.context_lens[s]), int(case.query_lens[s])
+        q0 = int(case.query_start_loc[s])
+        rows = np.sort(rng.choice(L, size=16, replace=False))
+        rows[0], rows[-1] = 0, L - 1
+        for i in rows:
+            ref = oracle.prefill_ref(case.query[q0 + i:q0 + i + 1], case.pool.key_cache,
+                                     case.pool.value_cache, case.pool.block_tables[s:s + 1],
+                                     np.array([0, 1], np.int32), np.array([n - L + i + 1], np.int32),
+                                     case.block_size, case.scale, "bf16")
+            assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
