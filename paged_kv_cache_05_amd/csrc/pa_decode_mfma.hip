@@ -22,8 +22,9 @@
 //     tile in registers with v_perm_b32.
 //   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group), so
 //   the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
-// Softmax state: running max per head, shared by the four lanes holding that head (two
-// cross-row shuffles per chunk); accumulators are rescaled only when some head's max grows.
+// Softmax state: a running reference point per head, shared by the four lanes holding that head
+// (two cross-row shuffles per chunk for the chunk max); accumulators are rescaled only when
+// some head's max passes its reference point by more than 2^8.
 // Partitions, wave interleaving, prefetch and the final merge follow the vector-ALU kernel.
 #include "pa_common.h"
 
@@ -63,6 +64,8 @@ template <> struct Mfma<DT::F16> {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
   }
 };
+
+constexpr float kLazy = 8.0f;   // running-max slack (log2 units): probabilities < 256
 
 template <DT dt, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
@@ -196,10 +199,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
+    // Lazy reference point: it moves only when a head's max exceeds it by more than kLazy
+    // (always on the first live chunk, from -inf), so probabilities stay below 2^kLazy and the
+    // rescale -- four cross-lane shuffles and 32 multiplies -- runs on few chunks instead of on
+    // every chunk that sets a new max.  Any reference point gives the same o / l.
     const float mn = fmaxf(m_run, bm);
-    const float ms = safe_max(mn);
-    if (__any(mn != m_run)) {
-      const float alpha = fast_exp2(m_run - ms);
+    const bool grow = mn > m_run + kLazy;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - mn) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -207,8 +214,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e][i] *= a;
       }
+      m_run = grow ? mn : m_run;
     }
-    m_run = mn;
+    const float ms = safe_max(m_run);
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
