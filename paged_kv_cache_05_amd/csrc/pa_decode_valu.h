@@ -11,7 +11,8 @@
 // partition of P tokens).  Splitting one sequence over partitions is what lets long contexts
 // spread over all 256 CUs; the partial results are merged exactly by their log-sum-exp
 // weights (pa_merge.hip).  A partition is cut into 16-token chunks; wave w takes chunks w,
-// w+4, w+8, ...
+// w+4, w+8, ...  A chunk is a slice of one block (blocks of 16 tokens and more) or two whole
+// 8-token blocks, each with its own table entry.
 //
 // Data path for one chunk.  A (block, KV head) tile is block_size * head_dim contiguous
 // elements.  One 16-byte load per lane moves 1 KiB per wave: with LPT = head_dim*elem/16 lanes
