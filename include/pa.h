@@ -123,8 +123,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *                 NULL when that is 0); contents on entry are ignored
  *
  * Supported: block_size in {8, 16, 32, 64, 128}; head_dim 64 or 128 for every 16/32-bit
- * pa_dtype, and also 80 or 256 for PA_F16 / PA_BF16; num_heads a multiple of num_kv_heads.  Slots past a sequence's context, unused blocks and unused
- * table entries are never read as values, so they may hold anything (NaN included).
+ * pa_dtype, and also 80 or 256 for PA_F16 / PA_BF16; num_heads a multiple of num_kv_heads;
+ * num_seqs * num_heads below 2^31 (otherwise PA_ERR_BAD_SHAPE).  Slots past a sequence's
+ * context, unused blocks and unused table entries are never read as values, so they may hold
+ * anything (NaN included).
  * Errors: PA_ERR_NULL_PTR, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE,
  * PA_ERR_LAUNCH.
  */

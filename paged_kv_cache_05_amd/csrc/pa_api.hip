@@ -49,6 +49,7 @@ pa_status check_shape(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
                       int32_t partition_size) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || maxb <= 0 || partition_size < 0) return PA_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return PA_ERR_BAD_SHAPE;
+  if ((long)S * Hq > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;   // (sequence, head) ids are int32
   if (D != 64 && D != 80 && D != 128 && D != 256) return PA_ERR_UNSUPPORTED;
   if (BS != 8 && BS != 16 && BS != 32 && BS != 64 && BS != 128) return PA_ERR_UNSUPPORTED;
   // partitions hold whole blocks and whole 16-token chunks

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     if (nparts == 1) {
       *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * 8) * EB) = Elem<dt>::pack(O);
     } else {
-      const size_t slot = (size_t)(s * p.num_heads + h0 + h) * p.max_parts + part;
+      const size_t slot = ((size_t)s * p.num_heads + h0 + h) * p.max_parts + part;
       float* po = p.ws_o + slot * D + cc * 8;
       *reinterpret_cast<float4*>(po) = make_float4(O[0], O[1], O[2], O[3]);
       *reinterpret_cast<float4*>(po + 4) = make_float4(O[4], O[5], O[6], O[7]);

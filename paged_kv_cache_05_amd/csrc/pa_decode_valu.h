@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
         *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * EPL) * Q::kBytes + 16 * v) =
             Q::pack(O + v * Q::kPerVec);
     } else {
-      const size_t slot = (size_t)(s * p.num_heads + h0 + h) * p.max_parts + part;
+      const size_t slot = ((size_t)s * p.num_heads + h0 + h) * p.max_parts + part;
       float* po = p.ws_o + slot * D + cc * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)

@@ -53,6 +53,7 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, bt=0) == 1
     assert _decode(lib, Hq=6, Hkv=4) == 2            # PA_ERR_BAD_SHAPE: heads not a multiple
     assert _decode(lib, S=-1) == 2
+    assert _decode(lib, S=2**26, Hq=64, Hkv=64) == 2   # (sequence, head) ids past int32
     assert _decode(lib, maxb=0) == 2
     assert _decode(lib, NB=0) == 2
     assert _decode(lib, P=24) == 2                   # not a multiple of block_size
