@@ -107,6 +107,15 @@ int heads_per_wg(bool mfma, int G, int D) {
   return 1;
 }
 
+// Grid of the vector-ALU decode: one workgroup per (partition, sequence, KV head, head chunk),
+// padded to a multiple of 8 x head chunks for the kernel's XCD-aware numbering (the padding
+// workgroups fall past the last partition and exit at once).
+long valu_grid(long S, long Hkv, long HC, long parts) {
+  long g = S * Hkv * HC * parts;
+  if (HC > 1) g = (g + 8 * HC - 1) / (8 * HC) * (8 * HC);
+  return g;
+}
+
 pa_status launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
 // Device block-engine state from the ABI arguments.
@@ -222,11 +231,14 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   p.scale_log2 = scale * 1.4426950408889634f;
   p.v_scale = 1.0f;
 
-  const long grid = (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts;
+  const long grid = mfma ? (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts
+                        : valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
+  // K/V read by several workgroups (a shared prefix, or several head chunks of one KV head)
+  // use cache-allocating loads, so the later readers find them in L2
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0 && p.head_chunks == 1;
   const hipError_t e = mfma ? pa::launch_decode_mfma(dt, head_dim, block_size, gt, stream_kv, p, (int)grid, s)
                             : pa::launch_decode_valu(dt, head_dim, block_size, gt, stream_kv, p, (int)grid, s);
   return launch_status(e);
@@ -472,10 +484,12 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   p.max_parts = pl.max_parts;
   p.scale_log2 = scale * k_scale * 1.4426950408889634f;
   p.v_scale = v_scale;
-  const long grid = (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts;
+  const long grid = valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
   (void)hipGetLastError();
-  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0;
+  // K/V read by several workgroups (a shared prefix, or several head chunks of one KV head)
+  // use cache-allocating loads, so the later readers find them in L2
+  const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0 && p.head_chunks == 1;
   return launch_status(pa::launch_decode_valu_fp8(dt, head_dim, block_size, gt, stream_kv, p,
                                                   (int)grid,
                                                   reinterpret_cast<hipStream_t>(stream)));

@@ -66,15 +66,25 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int colc = act ? col : VC - 1;
 
   // Workgroups are dealt round-robin to the 8 XCDs (id mod 8).  The partition index is the
-  // slowest grid index so every XCD gets an even share of (sequence, head) units; with it
-  // fastest, XCD k would receive only partition k.
-  const int units = p.num_seqs * p.num_kv_heads * p.head_chunks;
-  const int part = blockIdx.x / units;
-  const int unit = blockIdx.x - part * units;
-  const int hc = unit % (p.num_kv_heads * p.head_chunks);
-  const int s = unit / (p.num_kv_heads * p.head_chunks);
-  const int g = hc / p.head_chunks;
-  const int h0 = g * p.group + (hc % p.head_chunks) * GT;
+  // slowest index of the work item so every XCD gets an even share of (sequence, KV head)
+  // units; with it fastest, XCD k would receive only partition k.  When a KV head's query
+  // heads take several workgroups (head chunks), those read the same K/V: their ids are 8
+  // apart (id = 8 * (HC * j + chunk) + x), so they run on one XCD at about the same time and
+  // the later ones find the tiles in that XCD's L2.  The grid is padded to a multiple of 8 HC;
+  // padding items fall past the last partition and exit.
+  const int HC = p.head_chunks;
+  int chunk = 0, item = blockIdx.x;
+  if (HC > 1) {
+    const int y = blockIdx.x >> 3;
+    chunk = y % HC;
+    item = (y / HC) * 8 + (blockIdx.x & 7);
+  }
+  const int ukv = p.num_seqs * p.num_kv_heads;
+  const int part = item / ukv;
+  const int r = item - part * ukv;
+  const int s = r / p.num_kv_heads;
+  const int g = r - s * p.num_kv_heads;
+  const int h0 = g * p.group + chunk * GT;
 
   // Loads that do not depend on the context length go first, so their latency overlaps the
   // read of context_lens: the query rows and the table entries of this wave's first chunks

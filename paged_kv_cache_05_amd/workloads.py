@@ -129,6 +129,9 @@ CONFIGS = {
     # the Llama-7B-shaped decode step over an 8-bit E4M3 cache (bf16 queries and new tokens)
     "llama7b_bs16_fp8": CaseSpec("llama7b_bs16_fp8", 3, 256, 32, 32, 128, "bf16", 16,
                                  ("lognormal", 700.0, 1.0, 16, 4096), kv_dtype="fp8"),
+    # the GQA long-context step over an 8-bit E4M3 cache
+    "gqa_long_fp8": CaseSpec("gqa_long_fp8", 4, 16, 32, 8, 128, "bf16", 16, ("uniform", 8192, 32768),
+                             partition_size=512, kv_dtype="fp8"),
 }
 
 
