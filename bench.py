@@ -41,7 +41,7 @@ METRIC = "paged decode attention achieved HBM GB/s (% of MI355X peak) + seq-head
 TRAFFIC_FILE = ROOT / "profiles" / "decode_traffic.json"
 KERNEL_SOURCES = {
     "valu": ["pa_decode_valu.h", "pa_decode_valu_bf16.hip", "pa_common.h"],
-    "mfma": ["pa_decode_mfma.hip", "pa_common.h"],
+    "mfma": ["pa_decode_mfma.h", "pa_decode_mfma.hip", "pa_common.h"],
 }
 
 
@@ -94,12 +94,13 @@ def cache_write_bytes(case) -> int:
 
 def chosen_kernel(case, requested: str) -> str:
     sp = case.spec
+    G = sp.num_heads // sp.num_kv_heads
+    grouped = sp.dtype in ("f16", "bf16") and sp.head_dim == 128 and G % 4 == 0
     if sp.kv_dtype == "fp8":
-        return "valu_fp8"
+        return "mfma_fp8" if grouped else "valu_fp8"
     if requested != "auto":
         return requested
-    G = sp.num_heads // sp.num_kv_heads
-    return "mfma" if (sp.dtype in ("f16", "bf16") and sp.head_dim == 128 and G % 4 == 0) else "valu"
+    return "mfma" if grouped else "valu"
 
 
 class Step:
@@ -417,7 +418,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
-    ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8,tiny",
+    ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8,gqa_long_fp8,tiny",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

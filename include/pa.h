@@ -303,7 +303,9 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key
  * out are dtype (PA_F16 or PA_BF16); pools are uint8 as above; partition_size, workspace
  * (pa_decode_workspace_bytes with the same sizes), flags and errors as pa_decode_ex.
  * pa_decode_fp8_partitions is its first launch (pa_decode_merge, with the same dtype, is the
- * second).  Supported: head_dim 128, block_size 8, 16, 32, 64 or 128.
+ * second).  Supported: head_dim 128, block_size 8, 16, 32, 64 or 128.  When num_heads /
+ * num_kv_heads is a multiple of 4 (and partition_size one of 16) the grouped heads run on the
+ * matrix cores, the codes converted exactly to dtype in registers; otherwise on the vector ALUs.
  */
 pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
                         const void* value_cache, const int32_t* block_tables,

@@ -462,7 +462,11 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
                             max_blocks_per_seq, partition_size);
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return PA_ERR_WORKSPACE;
   const int G = num_heads / num_kv_heads;
-  const int gt = std::min(heads_per_wg(false, G, head_dim), 2);   // 16 fp32 outputs per lane per head
+  // Grouped heads (a multiple of 4) run on the matrix cores, which read each K/V byte once per
+  // KV head; otherwise the vector-ALU kernel, at most 2 heads per workgroup (16 fp32 outputs
+  // per lane per head).
+  const bool mfma = mfma_eligible(dt, head_dim, G, pl.partition);
+  const int gt = mfma ? heads_per_wg(true, G, head_dim) : std::min(heads_per_wg(false, G, head_dim), 2);
 
   pa::DecodeParams p;
   p.out = out;
@@ -484,15 +488,18 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   p.max_parts = pl.max_parts;
   p.scale_log2 = scale * k_scale * 1.4426950408889634f;
   p.v_scale = v_scale;
-  const long grid = valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
+  const long grid = mfma ? (long)num_seqs * num_kv_heads * p.head_chunks * pl.max_parts
+                        : valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
   (void)hipGetLastError();
   // K/V read by several workgroups (a shared prefix, or several head chunks of one KV head)
   // use cache-allocating loads, so the later readers find them in L2
   const bool stream_kv = (flags & PA_DECODE_SHARED_BLOCKS) == 0 && p.head_chunks == 1;
-  return launch_status(pa::launch_decode_valu_fp8(dt, head_dim, block_size, gt, stream_kv, p,
-                                                  (int)grid,
-                                                  reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launch_status(mfma ? pa::launch_decode_mfma_fp8(dt, head_dim, block_size, gt, stream_kv, p,
+                                                         (int)grid, s)
+                            : pa::launch_decode_valu_fp8(dt, head_dim, block_size, gt, stream_kv, p,
+                                                         (int)grid, s));
 }
 
 pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,

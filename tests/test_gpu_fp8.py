@@ -63,6 +63,8 @@ MATRIX = [
     ("bf16", 64, 8, 8, (1, 63, 64, 65, 700), 128),    # 64-token blocks
     ("f16", 128, 4, 2, (1, 127, 129, 900), 0),        # 128-token blocks
     ("bf16", 8, 8, 2, (1, 7, 8, 9, 300), 16),         # 8-token blocks, one-chunk partitions
+    ("f16", 16, 16, 4, (1, 15, 17, 640, 333), 64),    # G = 4 with f16 queries (matrix cores)
+    ("bf16", 32, 16, 2, (5, 100, 1100), 0),           # G = 8: 8 heads per workgroup
 ]
 
 
@@ -82,10 +84,13 @@ def test_decode_fp8_matches_oracle(dtype, bs, Hq, Hkv, lengths, P):
     assert_attention_close(got, _oracle(case), dtype, _vmax(case, vdeq), "decode_fp8")
 
 
-def test_decode_fp8_poison_and_junk_tables():
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2)])
+def test_decode_fp8_poison_and_junk_tables(heads):
+    """NaN codes in every slot no sequence reads and junk table entries: same bits as the clean
+    run (vector-ALU kernel for G = 1, matrix cores for G = 4)."""
     import torch
     dev = need_gpu()
-    spec = _spec("bf16", 16, 4, 4, (1, 15, 16, 33, 100), seed=210, max_blocks_per_seq=12)
+    spec = _spec("bf16", 16, heads[0], heads[1], (1, 15, 16, 33, 100), seed=210, max_blocks_per_seq=12)
     outs = []
     for kw in ({}, {"poison": True, "table_fill": -1}, {"poison": True, "table_fill": 2**31 - 1}):
         case = W.build_case(spec, **kw)
