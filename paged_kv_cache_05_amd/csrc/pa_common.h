@@ -160,6 +160,18 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over the four lanes l, l^16, l^32, l^48 (one query row of an MFMA output).  Each
+// permlane swap leaves, in every lane, its own value and its partner's (lane ^ 32, then
+// lane ^ 16) in the two results, whichever result holds which.
+__device__ __forceinline__ float row_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Streaming 16-byte load: K/V tiles are read exactly once per call, so they are fetched with
 // the non-temporal hint and do not displace reusable lines in the caches.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));

@@ -26,7 +26,7 @@
 //   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group), so
 //   the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
 // Softmax state: a running reference point per head, shared by the four lanes holding that head
-// (two cross-row shuffles per chunk for the chunk max); accumulators are rescaled only when
+// (two permlane swaps per chunk for the chunk max); accumulators are rescaled only when
 // some head's max passes its reference point by more than 2^8.
 // Partitions, wave interleaving, prefetch and the final merge follow the vector-ALU kernel.
 #include <type_traits>
@@ -256,9 +256,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
         }
       }
     }
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    // chunk max per head over the four token groups (lanes l, l^16, l^32, l^48), with
+    // permlane swaps on the vector ALUs rather than LDS round trips
+    const float bm = row_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     // Lazy reference point: it moves only when a head's max exceeds it by more than kLazy
     // (always on the first live chunk, from -inf), so probabilities stay below 2^kLazy and the
     // rescale -- four cross-lane shuffles and 32 multiplies -- runs on few chunks instead of on

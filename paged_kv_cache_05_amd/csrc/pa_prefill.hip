@@ -84,18 +84,6 @@ constexpr float kLazy = 8.0f;    // running-max slack (log2 units): probabilitie
 
 __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
-// Max over the four lanes l, l^16, l^32, l^48 (one query row of an MFMA output).  Each
-// permlane swap leaves, in every lane, its own value and its partner's (lane ^ 32, then
-// lane ^ 16) in the two results, whichever result holds which.
-__device__ __forceinline__ float row_max4(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 template <DT dt, int BS, bool SPLIT_P>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParams p) {
   using M = Mma<dt>;
