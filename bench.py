@@ -232,8 +232,10 @@ def traffic_for(kernel, workload):
     return entry.get("hbm_bytes_per_launch")
 
 
-def calibrate_copy(dev, steps):
-    """copy_blocks over 4096 distinct 128 KiB blocks (K and V): 1 GiB read + 1 GiB written."""
+def copy_ceiling(dev, steps):
+    """copy_blocks over 4096 distinct 128 KiB blocks (K and V): 1 GiB read + 1 GiB written per
+    launch.  Returns (ms per launch, bytes read per launch); reported as the box's achievable
+    copy rate, context for the decode's read bandwidth."""
     import torch
     nb, shape = 8192, (8192, 32, 16, 128)
     kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
@@ -250,6 +252,13 @@ def calibrate_copy(dev, steps):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
     moved = 2 * (nb // 2) * 32 * 16 * 128 * 2
+    del kc, vc
+    return ms, moved
+
+
+def calibrate_copy(dev, steps):
+    """The copy of copy_ceiling, printed for the HBM-counter calibration runs."""
+    ms, moved = copy_ceiling(dev, steps)
     print(json.dumps({"calibration": "copy_blocks", "read_bytes_per_launch": moved,
                       "write_bytes_per_launch": moved, "ms_per_launch": round(ms, 4),
                       "GBps_read_plus_write": round(2 * moved / ms / 1e6, 1)}), flush=True)
@@ -539,6 +548,11 @@ def main(argv=None):
         del step
         torch.cuda.empty_cache()
         detail["swap_blocks"] = measure_swap(dev, max(3, args.steps // 4))
+        torch.cuda.empty_cache()
+        cms, cmoved = copy_ceiling(dev, max(3, args.steps // 2))
+        detail["copy_ceiling"] = {"what": "copy_blocks, 1 GiB read + 1 GiB written per launch",
+                                  "ms": round(cms, 4),
+                                  "GBps_read_plus_write": round(2 * cmoved / cms / 1e6, 1)}
         torch.cuda.empty_cache()
         for pname in ("prefill_llama7b", "prefill_gqa"):
             detail[pname] = measure_prefill(dev, pname, args.steps, args.warmup)
