@@ -234,7 +234,7 @@ def traffic_for(kernel, workload):
 
 def copy_ceiling(dev, steps):
     """copy_blocks over 4096 distinct 128 KiB blocks (K and V): 1 GiB read + 1 GiB written per
-    launch.  Returns (ms per launch, bytes read per launch); reported as the box's achievable
+    launch.  Returns (ms per launch, bytes read per launch); reported as the GPU's achievable
     copy rate, context for the decode's read bandwidth."""
     import torch
     nb, shape = 8192, (8192, 32, 16, 128)
