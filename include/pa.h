@@ -25,7 +25,8 @@
  *     on the host (that would need a synchronisation); the kernels still guard every index
  *     so that a bad one is skipped instead of read or written out of bounds.
  *   - `num_seqs`, `num_tokens` or `num_pairs` equal to 0 is a successful no-op.
- *   - The library is stateless apart from cached device properties; calls are thread-safe.
+ *   - The library keeps no state between calls; calls from several threads (on their own
+ *     streams) are safe.
  *
  * Element types: `pa_dtype` selects the element type of q, out, key, value and both pools
  * (all of one call share it).  Arithmetic is fp32 in every kernel.
