@@ -233,3 +233,18 @@ def test_very_long_context(kernel):
     ref = oracle_decode(c)
     for P in (512, 0):
         assert_attention_close(u.decode(kernel, P), ref, "bf16", live_vmax(c), f"long/{kernel}/P{P}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883, -2.0])
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_zero_and_negative_scale(kernel, scale):
+    """scale 0 weights every token equally (the mean of V); a negative scale reverses the
+    ordering of the scores -- both against the oracle, single pass and split."""
+    dev = need_gpu()
+    c = _case("bf16", 128, 16, 8, 2, lengths=[1, 17, 300, 1000], seed=21)
+    c.scale = np.float32(scale)
+    say(f"decode {kernel} scale={scale}")
+    u = Uploaded(c, dev)
+    ref = oracle_decode(c)
+    for P in (0, 64):
+        assert_attention_close(u.decode(kernel, P), ref, "bf16", live_vmax(c), f"scale {scale}/{kernel}/P{P}")

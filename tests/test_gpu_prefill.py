@@ -235,3 +235,15 @@ def test_prefill_long_chunks_sampled():
                                      np.array([0, 1], np.int32), np.array([n - L + i + 1], np.int32),
                                      case.block_size, case.scale, "bf16")
             assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883, -2.0])
+def test_prefill_zero_and_negative_scale(scale):
+    """The kernel takes row maxima on raw scores, so a negative scale is applied by flipping
+    the query signs and scale 0 by the smallest normal multiplier: both against the oracle."""
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec("bf16", 16, 8, 2, (0, 40, 300), (70, 1, 129), seed=22))
+    case.pool.scale = np.float32(scale)
+    say(f"prefill scale={scale}")
+    got = Prefill(case, dev).run()
+    assert_attention_close(got, oracle_prefill(case), "bf16", vmax_of(case), f"scale {scale}")
