@@ -309,8 +309,9 @@ def _lengths_str(spec_lengths) -> str:
 
 
 def measure_prefill(dev, name, steps, warmup):
-    """pa_prefill on a chunked-prefill workload, both probability precisions, timed with HIP
-    events on the launch stream."""
+    """pa_prefill_ex on a chunked-prefill workload (the library's key-split choice, workspace
+    allocated once), both probability precisions, timed with HIP events on the launch
+    stream."""
     import torch
     case = W.build_prefill_case(W.PREFILL_CONFIGS[name], device=dev)
     sp = case.spec
@@ -320,13 +321,16 @@ def measure_prefill(dev, name, steps, warmup):
     cl = torch.from_numpy(case.context_lens).to(dev)
     out = torch.empty_like(q)
     flops = prefill_flops(case)
+    need = ops.prefill_workspace_bytes(sp.num_seqs, q.shape[0], sp.num_heads, sp.num_kv_heads,
+                                       sp.head_dim, sp.block_size, bt.shape[1], case.max_query_len)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     res = {"flops_per_launch": flops, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
            "num_kv_heads": sp.num_kv_heads, "chunk": _lengths_str(sp.chunk_lengths),
-           "cached_prefix": str(sp.prefix_lengths)}
+           "cached_prefix": str(sp.prefix_lengths), "key_split_workspace_bytes": need}
     for mode, bf16_p in (("p16", False), ("p_bf16", True)):
         def run():
             ops.prefill(out, q, case.pool.key_cache, case.pool.value_cache, bt, qsl, cl,
-                        float(case.scale), case.max_query_len, bf16_p=bf16_p)
+                        float(case.scale), case.max_query_len, bf16_p=bf16_p, workspace=ws)
         for _ in range(max(warmup, 10)):
             run()
         torch.cuda.synchronize()

@@ -279,6 +279,37 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache, const 
                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
                      float scale, pa_dtype dtype, uint32_t flags, void* stream);
 
+
+/*
+ * pa_prefill_ex — pa_prefill with the keys of long contexts split over workgroups.  A grid of
+ * (sequence, KV head, 128-row tile) workgroups that would not fill the GPU for long (small
+ * batches over long cached prefixes) is also cut along the keys: split k covers key tiles
+ * [k * kv_split, (k + 1) * kv_split) of every row; a row whose keys span several splits gets
+ * one partial (max, denominator, normalised output) per split, combined by their log-sum-exp
+ * weights in a second launch (the decode merge).  The result equals pa_prefill's up to
+ * rounding order.
+ *   num_tokens   T, the rows of query and out (= query_start_loc[num_seqs])
+ *   kv_split     tokens per key split, a multiple of 64; 0 = library choice (split only
+ *                grids below ~1024 workgroups, at least 512 tokens per split); a value
+ *                covering the whole table means no split
+ *   workspace    device buffer of at least pa_prefill_workspace_bytes(...) bytes (may be
+ *                NULL when that is 0); contents on entry are ignored
+ * Errors as pa_prefill, plus PA_ERR_WORKSPACE for a missing or short workspace and
+ * PA_ERR_BAD_SHAPE for a kv_split that is negative or not a multiple of 64, or num_tokens
+ * < 1 when the keys are split.
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t max_query_len,
+                                  int32_t kv_split);
+pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                        float scale, pa_dtype dtype, int32_t kv_split, void* workspace,
+                        size_t workspace_bytes, uint32_t flags, void* stream);
 /*
  * 8-bit KV cache.  The cache element type is a serving choice (kv_cache_dtype in the vLLM
  * configuration on the yongjin360.com page, §3.2); an E4M3 cache halves the bytes decode

@@ -136,6 +136,48 @@ pa_status engine_of(int32_t* tables, int32_t* lens, int32_t* refs, int32_t* stac
   return PA_OK;
 }
 
+// Key-split plan of a prefill call.  Splitting is for grids too small to fill the GPU for
+// long: below kPrefillTargetWG workgroups the keys are cut so that the grid reaches about
+// that many, with at least kMinSplitTiles tiles per split (each split costs a partial write
+// and a merge read per row).  An explicit kv_split (tokens, a multiple of 64) overrides it.
+constexpr long kPrefillTargetWG = 2048;
+constexpr long kPrefillSplitBelow = 1024;
+constexpr long kMinSplitTiles = 8;
+
+struct PrefillPlan {
+  int kv_splits = 1, split_tiles = 0;
+  long row_tiles = 0;
+  size_t tok_bytes = 0, ml_bytes = 0, ws_bytes = 0;
+};
+
+pa_status prefill_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_query_len,
+                       int32_t num_tokens, int32_t kv_split, PrefillPlan* pl) {
+  if (kv_split < 0 || kv_split % 64 != 0) return PA_ERR_BAD_SHAPE;
+  const long G = num_heads / num_kv_heads;
+  pl->row_tiles = ((long)max_query_len * G + 127) / 128;
+  const long cap_tiles = ((long)max_blocks_per_seq * block_size + 63) / 64;
+  pl->split_tiles = (int)std::min<long>(cap_tiles, 0x7FFFFFFF);
+  const long base = (long)num_seqs * num_kv_heads * pl->row_tiles;
+  long st = cap_tiles;
+  if (kv_split > 0) {
+    st = kv_split / 64;
+  } else if (base > 0 && base < kPrefillSplitBelow) {
+    const long ks = std::min((kPrefillTargetWG + base - 1) / base, cap_tiles / kMinSplitTiles);
+    if (ks > 1) st = (cap_tiles + ks - 1) / ks;
+  }
+  const long ks = (cap_tiles + st - 1) / st;
+  if (ks <= 1) return PA_OK;
+  if (num_tokens <= 0) return PA_ERR_BAD_SHAPE;   // splitting needs the token count
+  pl->kv_splits = (int)ks;
+  pl->split_tiles = (int)st;
+  const size_t slots = (size_t)num_tokens * num_heads * ks;
+  pl->tok_bytes = align256((size_t)num_tokens * sizeof(int32_t));
+  pl->ml_bytes = align256(slots * 2 * sizeof(float));
+  pl->ws_bytes = pl->tok_bytes + pl->ml_bytes + slots * 128 * sizeof(float);
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,29 +405,49 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
-pa_status pa_prefill(void* out, const void* query, const void* key_cache, const void* value_cache,
-                     const int32_t* block_tables, const int32_t* query_start_loc,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
-                     float scale, pa_dtype dtype, uint32_t flags, void* stream) {
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t max_query_len,
+                                  int32_t kv_split) {
+  if (check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                  0) != PA_OK || head_dim != 128 || max_query_len < 0)
+    return 0;
+  PrefillPlan pl;
+  if (prefill_plan(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                   max_query_len, num_tokens, kv_split, &pl) != PA_OK)
+    return 0;
+  return pl.ws_bytes;
+}
+
+pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                        float scale, pa_dtype dtype, int32_t kv_split, void* workspace,
+                        size_t workspace_bytes, uint32_t flags, void* stream) {
   DT dt;
   if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
   pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                              max_blocks_per_seq, 0);
   if (st != PA_OK) return st;
-  if (max_query_len < 0) return PA_ERR_BAD_SHAPE;
+  if (max_query_len < 0 || num_tokens < 0) return PA_ERR_BAD_SHAPE;
   if (dt == DT::F32 || head_dim != 128) return PA_ERR_UNSUPPORTED;
   if ((flags & ~PA_PREFILL_BF16_P) != 0) return PA_ERR_UNSUPPORTED;
+  PrefillPlan pl;
+  st = prefill_plan(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                    max_query_len, num_tokens, kv_split, &pl);
+  if (st != PA_OK) return st;
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
   if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !query_start_loc ||
       !context_lens)
     return PA_ERR_NULL_PTR;
   if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return PA_ERR_WORKSPACE;
   const int G = num_heads / num_kv_heads;
-  const long row_tiles = ((long)max_query_len * G + 127) / 128;
-  const long grid = (long)num_seqs * num_kv_heads * row_tiles;
+  const long grid = (long)num_seqs * num_kv_heads * pl.row_tiles * pl.kv_splits;
   if (grid > 0x7FFFFFFFL || (long)max_query_len * G > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
 
   pa::PrefillParams p;
@@ -403,16 +465,54 @@ pa_status pa_prefill(void* out, const void* query, const void* key_cache, const 
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_blocks = num_blocks;
   p.max_query_len = max_query_len;
-  p.row_tiles = (int)row_tiles;
+  p.row_tiles = (int)pl.row_tiles;
   // The kernel takes the row max on raw scores, which needs a positive multiplier: a negative
   // scale flips the query signs instead (exact), and 0 becomes the smallest normal float
   // (every score then rounds to a zero exponent, as scale 0 requires).
   p.scale_log2 = std::max(std::fabs(scale) * 1.4426950408889634f, 1.17549435e-38f);
   p.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
+  p.kv_splits = pl.kv_splits;
+  p.split_tiles = pl.split_tiles;
+  p.num_tokens = num_tokens;
+  char* ws = reinterpret_cast<char*>(workspace);
+  p.tok_len = pl.kv_splits > 1 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  p.ws_ml = pl.kv_splits > 1 ? reinterpret_cast<float*>(ws + pl.tok_bytes) : nullptr;
+  p.ws_o = pl.kv_splits > 1 ? reinterpret_cast<float*>(ws + pl.tok_bytes + pl.ml_bytes) : nullptr;
   const bool split_p = !(dt == DT::BF16 && (flags & PA_PREFILL_BF16_P));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  return launch_status(pa::launch_prefill_mfma(dt, block_size, split_p, p, (int)grid,
-                                               reinterpret_cast<hipStream_t>(stream)));
+  hipError_t e = pa::launch_prefill_mfma(dt, block_size, split_p, p, (int)grid, s);
+  if (e != hipSuccess || pl.kv_splits == 1) return launch_status(e);
+  // combine the split partials: every query token is a "sequence" whose context is its
+  // position + 1, partitioned by the split length
+  pa::MergeParams m;
+  m.out = out;
+  m.context_lens = p.tok_len;
+  m.ws_ml = p.ws_ml;
+  m.ws_o = p.ws_o;
+  m.num_seqs = num_tokens;
+  m.num_heads = num_heads;
+  m.max_blocks_per_seq = max_blocks_per_seq;
+  m.block_size = block_size;
+  m.partition = pl.split_tiles * 64;
+  m.max_parts = pl.kv_splits;
+  return launch_status(pa::launch_merge(dt, head_dim, m, s));
+}
+
+pa_status pa_prefill(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const int32_t* block_tables, const int32_t* query_start_loc,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                     float scale, pa_dtype dtype, uint32_t flags, void* stream) {
+  // one pass over every key (no split, no workspace): a split length past the table
+  const long cap = (long)max_blocks_per_seq * block_size;
+  const int32_t no_split = (int32_t)std::min<long>((cap + 63) / 64 * 64, 0x7FFFFFC0L);
+  return pa_prefill_ex(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                       context_lens, num_seqs, 0, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_query_len, scale, dtype,
+                       max_blocks_per_seq > 0 && block_size > 0 ? std::max<int32_t>(no_split, 64) : 64,
+                       nullptr, 0, flags, stream);
 }
 
 pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,

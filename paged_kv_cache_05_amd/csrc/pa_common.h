@@ -247,6 +247,17 @@ struct PrefillParams {
   int32_t row_tiles;                // workgroups per (sequence, KV head): ceil(max_query_len * G / 128)
   float scale_log2;                 // |scale| * log2(e), at least FLT_MIN (so it is > 0)
   uint32_t q_sign;                  // 0x80008000 when scale < 0: query signs are flipped instead
+  // Key splits: each (sequence, KV head, row tile) is also cut into kv_splits workgroups over
+  // key tiles [k * split_tiles, (k + 1) * split_tiles).  With kv_splits > 1 a token whose keys
+  // span several splits gets per-split (max, denominator, normalised output) triples in
+  // ws_ml / ws_o ([token][head][kv_splits] like the decode partitions) and tok_len[token] =
+  // its position + 1 (0: leave the row to the prefill kernel or unwritten); the decode merge
+  // kernel then combines them.
+  int32_t kv_splits, split_tiles;
+  int32_t num_tokens;               // rows of the workspace arrays (writes past them are skipped)
+  int32_t* tok_len;
+  float* ws_ml;
+  float* ws_o;
 };
 
 // host-side launchers (return hipSuccess or the launch error)

@@ -96,15 +96,26 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lr = lane & 15, lg = lane >> 4;
 
-  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (id mod 8); renumbering gives
-  // each XCD a contiguous range of items, so the row tiles of one (sequence, KV head), which
-  // read the same K/V, share that XCD's L2.  Within a unit the last rows (longest causal
-  // range) come first.
-  const int total = p.num_seqs * p.num_kv_heads * p.row_tiles;
-  int w = blockIdx.x;
-  if ((total & 7) == 0) w = (w & 7) * (total >> 3) + (w >> 3);
-  const int unit = w / p.row_tiles;
-  const int rt = p.row_tiles - 1 - (w - unit * p.row_tiles);
+  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (id mod 8).  Unit u =
+  // (sequence, KV head) goes whole to XCD u mod 8 -- its row tiles and key splits, which read
+  // the same K/V, share that XCD's L2 and run one after another -- and the units are dealt
+  // round-robin, so every XCD gets the same KV heads of all sequences (units in contiguous
+  // blocks per XCD would give an XCD whole sequences, whose work can differ several-fold).
+  // Within a unit the last rows (longest causal range) come first, the key split fastest.
+  const int KS = p.kv_splits;
+  const int IPU = p.row_tiles * KS;                  // items per unit
+  const int units = p.num_seqs * p.num_kv_heads;
+  int unit, sub;
+  if ((units & 7) == 0) {
+    const int j = blockIdx.x >> 3;
+    unit = (j / IPU) * 8 + (blockIdx.x & 7);
+    sub = j - (j / IPU) * IPU;
+  } else {
+    unit = blockIdx.x / IPU;
+    sub = blockIdx.x - unit * IPU;
+  }
+  const int ks = sub % KS;
+  const int rt = p.row_tiles - 1 - sub / KS;
   const int kvh = unit % p.num_kv_heads;
   const int s = unit / p.num_kv_heads;
 
@@ -115,6 +126,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   const int G = p.group;
   const int rows = L * G;
   const int row0 = rt * kRowsWG;
+  const bool fits = n >= L_all && n <= p.max_blocks_per_seq * BS;
+  if (KS > 1 && kvh == 0 && rt == 0 && ks == 0) {
+    // token lengths for the merge: position + 1 for the rows this grid covers; 0 for rows
+    // written here directly (a chunk that does not fit: zeros) or left unwritten
+    for (int t = tid; t < L_all && q0 + t < p.num_tokens; t += 256)
+      p.tok_len[q0 + t] = (fits && t < L) ? n - L_all + t + 1 : 0;
+  }
   if (L <= 0 || row0 >= rows) return;
 
   // element offset of row r's query / output vector
@@ -123,7 +141,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
     return ((size_t)(q0 + t) * p.num_heads + kvh * G + (r - t * G)) * kD;
   };
 
-  if (n < L_all || n > p.max_blocks_per_seq * BS) {  // the chunk does not fit its context: zeros
+  if (!fits) {  // the chunk does not fit its context: zeros (from the first key split)
+    if (ks != 0) return;
     for (int idx = tid; idx < kRowsWG * 16; idx += 256) {
       const int r = row0 + (idx >> 4);
       if (r < rows)
@@ -135,7 +154,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 
   const int prefix = n - L_all;
   const int last_row = min(rows, row0 + kRowsWG) - 1;
-  const int ntiles = (prefix + last_row / G + 1 + kTile - 1) / kTile;
+  const int ntiles_all = (prefix + last_row / G + 1 + kTile - 1) / kTile;
+  const int k_begin = ks * p.split_tiles;                     // this split's key tiles
+  const int k_end = min(ntiles_all, k_begin + p.split_tiles);
+  if (k_begin >= k_end) return;
 
   const int wrow0 = row0 + wave * kRowsWave;
   const bool wave_active = wrow0 < rows;
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   const size_t blk_stride = (size_t)p.num_kv_heads * BS * kRow;
   auto entry = [&](int tile) -> int {
     const int page = (tile * kTile + 4 * tg) / BS;
-    return (tile < ntiles && page < nb_live) ? table[page] : -1;
+    return (tile < k_end && page < nb_live) ? table[page] : -1;
   };
   uint4 kr[4], vr[4];
   auto issue = [&](int tile, int ent) {
@@ -231,8 +253,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   f32x4 l_acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const uint4 ones = make_uint4(M::kOnes, M::kOnes, M::kOnes, M::kOnes);
 
-  int ent_next = entry(1);
-  issue(0, entry(0));
+  int ent_next = entry(k_begin + 1);
+  issue(k_begin, entry(k_begin));
   stash(0);
   __syncthreads();
 
@@ -297,7 +319,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
       alpha[c2] = grow ? fast_exp2(m_run[c2] - m_new) : 1.0f;
       m_run[c2] = m_new;
       any_grow |= grow;
-      const float neg_m = -m_new;
+      // a row with no key in this split yet keeps -inf: exp2(-inf) = 0, not NaN
+      const float neg_m = m_new == -INFINITY ? 0.0f : -m_new;
       float pv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(st[e >> 2][c2][e & 3], p.scale_log2, neg_m));
@@ -343,9 +366,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
     }
   };
 
-  for (int k = 0; k < ntiles; ++k) {
-    const int buf = k & 1;
-    const bool more = k + 1 < ntiles;
+  for (int k = k_begin; k < k_end; ++k) {
+    const int buf = (k - k_begin) & 1;
+    const bool more = k + 1 < k_end;
     const int ent_after = entry(k + 2);
     if (more) issue(k + 1, ent_next);
 
@@ -375,12 +398,15 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
 
   if (!wave_active) return;
   // Finalise: the four lanes holding a row add their denominators; lane l writes dims
-  // 16b + 4(l/16) .. +4 of its rows.
+  // 16b + 4(l/16) .. +4 of its rows.  A row whose keys all lie in one split is written here;
+  // otherwise each split with keys for it writes its partial triple for the merge.
+  const int split_len = p.split_tiles * kTile;
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
     const float inv = 1.0f / l_acc[c2][0];
     const int r = wrow0 + 16 * c2 + lr;
-    if (r < rows) {
+    const int np = KS == 1 ? 1 : (lim[c2] + split_len) / split_len;   // splits holding its keys
+    if (r < rows && np == 1 && ks == 0) {
       char* op = (char*)p.out + row_off(r) * 2;
 #pragma unroll
       for (int dt2 = 0; dt2 < 8; ++dt2) {
@@ -389,6 +415,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
                                     M::bits(v[2] * inv) | (M::bits(v[3] * inv) << 16));
         *reinterpret_cast<uint2*>(op + (16 * dt2 + 4 * lg) * 2) = w2;
       }
+    } else if (r < rows && np > 1 && ks < np && q0 + r / G < p.num_tokens) {
+      const size_t slot = (row_off(r) / kD) * KS + ks;
+      float* po = p.ws_o + slot * kD;
+#pragma unroll
+      for (int dt2 = 0; dt2 < 8; ++dt2) {
+        const f32x4 v = o[dt2][c2];
+        *reinterpret_cast<float4*>(po + 16 * dt2 + 4 * lg) =
+            make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      }
+      if (lg == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * slot) = make_float2(m_run[c2], l_acc[c2][0]);
     }
   }
 }

@@ -46,6 +46,9 @@ _SIGNATURES = {
     "pa_copy_blocks": (_c_int, [_p] * 3 + [_c_int] * 6 + [_p]),
     "pa_swap_blocks": (_c_int, [_p, _p, _c_int, _p, _p, _c_int, _p] + [_c_int] * 5 + [_p]),
     "pa_prefill": (_c_int, [_p] * 7 + [_c_int] * 8 + [_c_float, _c_int, ctypes.c_uint32, _p]),
+    "pa_prefill_workspace_bytes": (_c_size, [_c_int] * 9),
+    "pa_prefill_ex": (_c_int, [_p] * 7 + [_c_int] * 9 + [_c_float, _c_int, _c_int, _p, _c_size,
+                                                       ctypes.c_uint32, _p]),
     "pa_append_slots": (_c_int, [_p] * 5 + [_c_int] * 4 + [_p, _c_int] + [_p] * 4 + [_p]),
     "pa_fork_seqs": (_c_int, [_p] * 3 + [_c_int] * 4 + [_p, _c_int, _p]),
     "pa_free_seqs": (_c_int, [_p] * 5 + [_c_int] * 4 + [_p, _c_int, _p]),
@@ -272,14 +275,23 @@ def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping, *, stream
 PA_PREFILL_BF16_P = 0x1
 
 
+def prefill_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, max_query_len, kv_split=0) -> int:
+    return int(load().pa_prefill_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                                 head_dim, block_size, max_blocks_per_seq,
+                                                 max_query_len, kv_split))
+
+
 def prefill(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens, scale,
-            max_query_len, *, bf16_p=False, stream=None):
-    """pa_prefill: causal attention of each sequence's chunk of new tokens over the paged cache.
+            max_query_len, *, bf16_p=False, kv_split=0, workspace=None, stream=None):
+    """pa_prefill_ex: causal attention of each sequence's chunk of new tokens over the paged
+    cache.
 
     ``query``/``out`` [T, Hq, d] hold the chunks back to back; sequence s owns rows
     ``query_start_loc[s] .. query_start_loc[s+1]-1`` (int32 [S+1]); ``context_lens`` (int32 [S])
     counts the cached tokens including the chunk.  ``max_query_len`` is a host integer no
-    smaller than any chunk.  ``bf16_p`` sets PA_PREFILL_BF16_P."""
+    smaller than any chunk.  ``bf16_p`` sets PA_PREFILL_BF16_P.  ``kv_split``: tokens per key
+    split (0: the library's choice); the workspace is allocated here when not given."""
     import torch
     dev = _dev(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens)
     T, Hq, D = query.shape
@@ -296,11 +308,17 @@ def prefill(out, query, key_cache, value_cache, block_tables, query_start_loc, c
         raise TypeError("block_tables, query_start_loc and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start_loc.shape) != (S + 1,):
         raise ValueError("block_tables must be [S, max_blocks] and query_start_loc [S + 1]")
-    _check(load().pa_prefill(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
-                             _ptr(block_tables), _ptr(query_start_loc), _ptr(context_lens), S, Hq,
-                             Hkv, D, BS, NB, block_tables.shape[1], int(max_query_len),
-                             float(scale), _dtype_code(query),
-                             PA_PREFILL_BF16_P if bf16_p else 0, _stream(dev, stream)), "pa_prefill")
+    maxb = block_tables.shape[1]
+    need = prefill_workspace_bytes(S, T, Hq, Hkv, D, BS, maxb, int(max_query_len), int(kv_split))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(load().pa_prefill_ex(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                _ptr(block_tables), _ptr(query_start_loc), _ptr(context_lens), S,
+                                T, Hq, Hkv, D, BS, NB, maxb, int(max_query_len), float(scale),
+                                _dtype_code(query), int(kv_split), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0,
+                                PA_PREFILL_BF16_P if bf16_p else 0, _stream(dev, stream)),
+           "pa_prefill_ex")
     return out
 
 

@@ -133,6 +133,40 @@ def _prefill(lib, **kw):
                           a["maxb"], a["maxq"], a["scale"], a["dtype"], a["flags"], None)
 
 
+def _prefill_ex(lib, **kw):
+    a = dict(out=1, q=1, kc=1, vc=1, bt=1, qsl=1, cl=1, S=4, T=100, Hq=8, Hkv=2, D=128, BS=16,
+             NB=100, maxb=64, maxq=64, scale=0.1, dtype=2, split=0, ws=0, wsb=0, flags=0)
+    a.update(kw)
+    p = lambda v: ctypes.c_void_p(v) if v else None
+    return lib.pa_prefill_ex(p(a["out"]), p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]),
+                             p(a["qsl"]), p(a["cl"]), a["S"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                             a["BS"], a["NB"], a["maxb"], a["maxq"], a["scale"], a["dtype"],
+                             a["split"], p(a["ws"]), a["wsb"], a["flags"], None)
+
+
+def test_prefill_split_plan_and_errors(lib):
+    """Key splits: the workspace query, the library's choice (split only small grids), an
+    explicit split length, and the argument errors of pa_prefill_ex."""
+    ws = lib.pa_prefill_workspace_bytes
+    # 4 seqs x 2 KV heads x 4 row tiles = 32 workgroups over 1024-token tables: split
+    auto = ws(4, 100, 8, 2, 128, 16, 64, 64, 0)
+    assert auto > 0
+    # 256 x 32 heads x 4 row tiles: the grid fills the GPU, no split
+    assert ws(256, 100, 32, 32, 128, 16, 64, 512, 0) == 0
+    assert ws(4, 100, 8, 2, 128, 16, 64, 64, 1024) == 0          # one split covers the table
+    two = ws(4, 100, 8, 2, 128, 16, 64, 64, 512)                 # two splits: 100 x 8 x 2 slots
+    # token lengths (400 B -> 512), (max, denominator) pairs, fp32 partial outputs
+    assert two == 512 + 1600 * 2 * 4 + 1600 * 128 * 4
+    assert ws(4, 100, 8, 2, 128, 16, 64, 64, 96) == 0            # not a multiple of 64
+    assert _prefill_ex(lib, split=96) == 2                       # PA_ERR_BAD_SHAPE
+    assert _prefill_ex(lib, split=-64) == 2
+    assert _prefill_ex(lib, T=0) == 2                            # splitting needs the token count
+    assert _prefill_ex(lib, T=0, split=1024, out=0) == 1         # no split: T unused
+    assert _prefill_ex(lib, split=512, ws=1, wsb=two - 1) == 4   # PA_ERR_WORKSPACE
+    assert _prefill_ex(lib, split=512) == 4                      # no workspace at all
+    assert _prefill_ex(lib, split=512, ws=1, wsb=two, out=0) == 1
+
+
 def test_prefill_argument_errors(lib):
     assert _prefill(lib, qsl=0) == 1                 # PA_ERR_NULL_PTR
     assert _prefill(lib, out=0) == 1

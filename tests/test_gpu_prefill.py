@@ -38,14 +38,14 @@ class Prefill:
         self.cl = torch.from_numpy(np.ascontiguousarray(case.context_lens, np.int32)).to(dev)
         self.out = torch.empty_like(self.q)
 
-    def run(self, bf16_p=False, max_query_len=None, context_lens=None, fill=None):
+    def run(self, bf16_p=False, max_query_len=None, context_lens=None, fill=None, kv_split=0):
         import torch
         if fill is not None:
             self.out.view(torch.int16 if self.out.element_size() == 2 else torch.int32).fill_(fill)
         ops.prefill(self.out, self.q, self.kc, self.vc, self.bt, self.qsl,
                     self.cl if context_lens is None else context_lens, float(self.case.scale),
                     self.case.max_query_len if max_query_len is None else max_query_len,
-                    bf16_p=bf16_p)
+                    bf16_p=bf16_p, kv_split=kv_split)
         torch.cuda.synchronize()
         return W.from_torch(self.out, self.case.dtype)
 
@@ -247,3 +247,99 @@ def test_prefill_zero_and_negative_scale(scale):
     say(f"prefill scale={scale}")
     got = Prefill(case, dev).run()
     assert_attention_close(got, oracle_prefill(case), "bf16", vmax_of(case), f"scale {scale}")
+
+
+SPLIT_MATRIX = [
+    # dtype, block size, Hq, Hkv, cached prefixes, chunk lengths, split tokens
+    ("bf16", 16, 4, 4, (0, 5, 100, 37), (1, 17, 130, 64), 64),
+    ("f16", 32, 8, 2, (0, 90, 17, 640), (40, 3, 100, 33), 128),
+    ("bf16", 16, 16, 2, (10, 0, 1290), (20, 47, 9), 320),
+    ("bf16", 8, 8, 2, (0, 7, 8, 501), (9, 1, 64, 70), 192),
+    ("bf16", 64, 2, 1, (0, 0), (300, 257), 64),
+]
+
+
+@pytest.mark.parametrize("dtype,bs,Hq,Hkv,prefix,chunk,kv_split", SPLIT_MATRIX)
+def test_prefill_key_splits(dtype, bs, Hq, Hkv, prefix, chunk, kv_split):
+    """Keys cut into splits of kv_split tokens (rows spanning several splits go through the
+    partial triples and the log-sum-exp merge; rows inside one split are written directly):
+    against the oracle, and the bf16-probabilities mode with splits against its own bound."""
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec(dtype, bs, Hq, Hkv, prefix, chunk, seed=300 + sum(chunk)))
+    say(f"prefill split {kv_split}: {dtype} bs{bs} Hq{Hq} Hkv{Hkv} prefix={prefix} chunk={chunk}")
+    run = Prefill(case, dev)
+    ref = oracle_prefill(case)
+    assert_attention_close(run.run(kv_split=kv_split), ref, dtype, vmax_of(case), f"split {kv_split}")
+    if dtype == "bf16":
+        ref_r = oracle.storage_to_f64(oracle.f64_to_storage(ref, "bf16"), "bf16")
+        g = oracle.storage_to_f64(run.run(kv_split=kv_split, bf16_p=True), "bf16")
+        rel = np.linalg.norm(g - ref_r) / np.linalg.norm(ref_r)
+        assert rel <= 4e-3 and np.max(np.abs(g - ref_r)) <= 1e-2 * vmax_of(case)
+
+
+def test_prefill_key_splits_invalid_and_clamped_rows():
+    """With splits, an over-long chunk still gives zero rows, rows past max_query_len keep
+    the sentinel, and the other rows match the unsplit result within the bar."""
+    import torch
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec("f16", 16, 4, 4, (5, 0, 9, 700), (30, 0, 12, 40), seed=23))
+    run = Prefill(case, dev)
+    ref = oracle_prefill(case)
+    lens = case.context_lens.copy()
+    lens[2] = 11
+    got = run.run(context_lens=torch.from_numpy(lens).to(dev), fill=0x7C01, kv_split=128)
+    r2 = slice(int(case.query_start_loc[2]), int(case.query_start_loc[3]))
+    assert np.all(oracle.storage_to_f64(got[r2], "f16") == 0.0)
+    keep = np.ones(got.shape[0], bool)
+    keep[r2] = False
+    assert_attention_close(got[keep], ref[keep], "f16", vmax_of(case), "split, other rows")
+    got = run.run(max_query_len=32, fill=0x7C01, kv_split=128)
+    r3 = int(case.query_start_loc[3])
+    assert np.all(bits(got[r3 + 32:r3 + 40], "f16") == 0x7C01)
+    assert_attention_close(got[:r3 + 32], ref[:r3 + 32], "f16", vmax_of(case), "split, clamped")
+
+
+def test_prefill_library_split_choice():
+    """A small grid over long prefixes: the library splits the keys by itself (a workspace is
+    needed) and the result matches the oracle."""
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec("bf16", 16, 8, 2, (2000, 1500), (100, 60), seed=24))
+    sp = case.spec
+    need = ops.prefill_workspace_bytes(sp.num_seqs, case.query.shape[0], sp.num_heads,
+                                       sp.num_kv_heads, 128, 16, case.pool.block_tables.shape[1],
+                                       case.max_query_len, 0)
+    assert need > 0
+    say(f"prefill, library split choice: workspace {need} bytes")
+    assert_attention_close(Prefill(case, dev).run(), oracle_prefill(case), "bf16", vmax_of(case),
+                           "library split")
+
+
+def test_prefill_gqa_full_size_sampled():
+    """The GQA chunked-prefill workload (8 sequences, ragged chunks on up to 3000 cached
+    tokens), run as the benchmark runs it (the library splits its keys); sampled rows of
+    three sequences against the oracle on one-row chunks."""
+    import torch
+    dev = need_gpu()
+    spec = W.PREFILL_CONFIGS["prefill_gqa"]
+    case = W.build_prefill_case(spec, device=dev)
+    say(f"prefill full size: {spec.name}")
+    got = Prefill(case, dev).run()
+    assert np.all(np.isfinite(oracle.storage_to_f64(got, "bf16")))
+    rng = np.random.default_rng(25)
+    bs = spec.block_size
+    for s in (0, 3, 7):
+        n = int(case.context_lens[s])
+        L = int(case.query_lens[s])
+        nb = -(-n // bs)
+        ids = torch.from_numpy(case.pool.block_tables[s, :nb].astype(np.int64)).to(dev)
+        kc = W.from_torch(case.pool.key_cache.index_select(0, ids), "bf16")
+        vc = W.from_torch(case.pool.value_cache.index_select(0, ids), "bf16")
+        table = np.arange(nb, dtype=np.int32)[None]
+        rows = np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=min(L, 12), replace=False)]))
+        q0 = int(case.query_start_loc[s])
+        vmax = float(np.max(np.abs(oracle.storage_to_f64(vc, "bf16"))))
+        for i in rows:
+            ref = oracle.prefill_ref(case.query[q0 + i:q0 + i + 1], kc, vc, table,
+                                     np.array([0, 1], np.int32),
+                                     np.array([n - L + i + 1], np.int32), bs, case.scale, "bf16")
+            assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
