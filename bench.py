@@ -436,7 +436,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b_bs16", choices=sorted(W.CONFIGS))
     ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8,gqa_long_fp8,tiny",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
