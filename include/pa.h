@@ -413,6 +413,7 @@ pa_status pa_free_seqs(int32_t* block_tables, int32_t* context_lens, int32_t* re
 /*
  * pa_copy_blocks_counted — pa_copy_blocks with the pair count read on the device
  * (*num_pairs, as pa_append_slots writes it); max_pairs bounds it and sizes the launch.
+ * block_mapping must hold max_pairs readable rows (rows past *num_pairs are read, not used).
  */
 pa_status pa_copy_blocks_counted(void* key_cache, void* value_cache, const int64_t* block_mapping,
                                  const int32_t* num_pairs, int32_t max_pairs,

@@ -85,8 +85,10 @@ __global__ __launch_bounds__(256) void block_copy_kernel(const uint4* __restrict
   const int chunk = blockIdx.x % chunks;
   const int which = (blockIdx.x / chunks) & 1;
   const int pair = blockIdx.x / (2 * chunks);
-  if (count != nullptr && pair >= *count) return;   // pair count produced on the device
+  // the pair's ids are read together with the device-made count (the mapping always holds
+  // as many rows as the grid has pairs), saving one dependent round trip
   const int64_t src = mapping[2 * pair], dst = mapping[2 * pair + 1];
+  if (count != nullptr && pair >= *count) return;   // pair count produced on the device
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const uint4* s = (which ? src_v : src_k) + src * block_vecs;
   uint4* d = (which ? dst_v : dst_k) + dst * block_vecs;

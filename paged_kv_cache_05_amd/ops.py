@@ -457,9 +457,12 @@ def free_seqs(block_tables, context_lens, ref_counts, free_stack, free_top, seq_
 
 
 def copy_blocks_counted(key_cache, value_cache, block_mapping, num_pairs, max_pairs, *, stream=None):
-    """pa_copy_blocks_counted: the pair count is read from num_pairs (int32 [1], on the GPU)."""
+    """pa_copy_blocks_counted: the pair count is read from num_pairs (int32 [1], on the GPU);
+    block_mapping (int64 [>= max_pairs, 2]) holds max_pairs readable rows."""
     dev = _dev(key_cache, value_cache, block_mapping, num_pairs)
     NB, Hkv, BS, D = key_cache.shape
+    if block_mapping.numel() < 2 * int(max_pairs):
+        raise ValueError("block_mapping must hold max_pairs rows")
     _check(load().pa_copy_blocks_counted(_ptr(key_cache), _ptr(value_cache), _ptr(block_mapping),
                                          _ptr(num_pairs), int(max_pairs), Hkv, D, BS, NB,
                                          _dtype_code(key_cache), _stream(dev, stream)),
