@@ -214,9 +214,18 @@ def snapshot_sequences(case, seqs):
     return out
 
 
-def cpu_baseline(case, snaps, budget_s):
-    """The float64 oracle decoding the snapshotted sequences one at a time (BLAS limited to one
-    thread), cycling over them until at least one full pass and ``budget_s`` seconds are done."""
+def host_threads() -> int:
+    """Host cores this process may use (its affinity mask), at most 16 (the share of one GPU)."""
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def cpu_baseline(case, snaps, budget_s, threads=1):
+    """The float64 oracle decoding the snapshotted sequences one at a time (BLAS limited to
+    ``threads`` threads), cycling over them until at least one full pass and ``budget_s``
+    seconds are done."""
     import oracle
     from threadpoolctl import threadpool_limits
     sp = case.spec
@@ -230,7 +239,7 @@ def cpu_baseline(case, snaps, budget_s):
                                               mk, mv, slot, bs)   # the step's write (untimed)
         prepared.append((s, n, mk, mv, table))
     done, bytes_done, heads, tokens, elapsed = 0, 0, 0, 0, 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         while done < len(prepared) or elapsed < budget_s:
             s, n, mk, mv, table = prepared[done % len(prepared)]
             t = time.perf_counter()
@@ -241,12 +250,12 @@ def cpu_baseline(case, snaps, budget_s):
             heads += sp.num_heads
             tokens += n
             done += 1
-    return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+    return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seq_heads_per_s": round(heads / elapsed, 2),
             "seconds": round(elapsed, 2),
             "sample": f"{done} sequence decodes cycling over the {len(prepared)} sequences of the "
                       f"step ({tokens} cached tokens read, all {sp.num_heads} heads each), numpy "
-                      f"float64, one BLAS thread"}
+                      f"float64, {threads} BLAS thread{'s' if threads > 1 else ''}"}
 
 
 def traffic_for(kernel, workload):
@@ -606,7 +615,12 @@ def main(argv=None):
         detail["shared_prefix_device_engine"] = measure_device_engine(dev, args.steps, args.warmup)
         rec["detail"] = detail
     if snaps is not None:
-        rec["cpu_baseline"] = cpu_baseline(case, snaps, args.cpu_seconds)
+        # the host's cores (BLAS threads), plus a one-thread timing for context
+        nt = host_threads()
+        rec["cpu_baseline"] = cpu_baseline(case, snaps, 0.6 * args.cpu_seconds, nt)
+        if nt > 1:
+            one = cpu_baseline(case, snaps, 0.4 * args.cpu_seconds, 1)
+            rec["cpu_baseline"]["one_thread"] = {k: one[k] for k in ("value", "seq_heads_per_s", "seconds")}
     print(json.dumps(rec), flush=True)
     return 0
 
