@@ -144,6 +144,24 @@ def _prefill_ex(lib, **kw):
                              a["split"], p(a["ws"]), a["wsb"], a["flags"], None)
 
 
+def test_plain_decode_argument_errors(lib):
+    """pa_decode (the basic entry) checks its arguments like pa_decode_ex."""
+    p = lambda v: ctypes.c_void_p(v) if v else None
+
+    def call(**kw):
+        a = dict(out=1, q=1, kc=1, vc=1, bt=1, cl=1, S=4, Hq=8, Hkv=2, D=128, BS=16, NB=100,
+                 maxb=8, scale=0.1, dtype=2, P=0, ws=0, wsb=0)
+        a.update(kw)
+        return lib.pa_decode(p(a["out"]), p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), p(a["cl"]),
+                             a["S"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"], a["maxb"],
+                             a["scale"], a["dtype"], a["P"], p(a["ws"]), a["wsb"], None)
+    assert call(out=0) == 1
+    assert call(Hq=6, Hkv=4) == 2
+    assert call(D=96) == 3
+    assert call(P=16, maxb=64) == 4                 # split: a workspace is needed
+    assert call(S=0) == 0
+
+
 def test_prefill_split_plan_and_errors(lib):
     """Key splits: the workspace query, the library's choice (split only small grids), an
     explicit split length, and the argument errors of pa_prefill_ex."""

@@ -248,3 +248,32 @@ def test_zero_and_negative_scale(kernel, scale):
     ref = oracle_decode(c)
     for P in (0, 64):
         assert_attention_close(u.decode(kernel, P), ref, "bf16", live_vmax(c), f"scale {scale}/{kernel}/P{P}")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,P", [("bf16", 8, 8, 0), ("f16", 8, 2, 64), ("f32", 4, 2, 48)])
+def test_plain_pa_decode_entry(dtype, Hq, Hkv, P):
+    """pa_decode (the basic entry: library-chosen kernel, caller's workspace) called directly
+    through the C ABI: same bits as pa_decode_ex with the automatic kernel, within the bar of
+    the oracle."""
+    import ctypes
+    import torch
+    from paged_kv_cache_05_amd import ops
+    dev = need_gpu()
+    c = _case(dtype, 64 if dtype == "f32" else 128, 16, Hq, Hkv, lengths=[1, 40, 600, 129], seed=33)
+    u = Uploaded(c, dev)
+    sp = c.spec
+    lib = ops.load()
+    nbytes = lib.pa_decode_workspace_bytes(sp.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim,
+                                           sp.block_size, c.max_blocks_per_seq, P)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(u.q)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.pa_decode(ptr(out), ptr(u.q), ptr(u.kc), ptr(u.vc), ptr(u.bt), ptr(u.cl), sp.num_seqs,
+                       sp.num_heads, sp.num_kv_heads, sp.head_dim, sp.block_size, c.num_blocks,
+                       c.max_blocks_per_seq, float(c.scale), ops._dtype_code(u.q), P, ptr(ws),
+                       ws.numel(), ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    assert st == 0, ops.status_string(st)
+    torch.cuda.synchronize()
+    got = W.from_torch(out, dtype)
+    assert np.array_equal(bits(got, dtype), bits(u.decode("auto", P), dtype))
+    assert_attention_close(got, oracle_decode(c), dtype, live_vmax(c), "pa_decode")
