@@ -202,3 +202,30 @@ def test_decode_fp8_full_size_sampled():
                                     np.array([n], np.int32), 16, case.scale, "bf16", K_SCALE, V_SCALE)
         vmax = float(np.max(np.abs(oracle.dequantize_fp8(vc, V_SCALE))))
         assert_attention_close(got[s:s + 1], ref, "bf16", vmax, f"seq {s} (n={n})")
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)])
+def test_decode_fp8_two_launches_equal_one(heads):
+    """pa_decode_fp8_partitions followed by pa_decode_merge (the two launches the benchmark
+    brackets with events) give the same bits as pa_decode_fp8, for the vector-ALU (G = 1) and
+    matrix-core (G = 4) paths, split and single pass."""
+    import torch
+    dev = need_gpu()
+    case = W.build_case(_spec("bf16", 16, heads[0], heads[1], (5, 300, 1200, 17), seed=230))
+    q, kc, vc, bt, cl = _upload(case, dev)
+    sp = case.spec
+    for P in (0, 64, 256):
+        say(f"fp8 two launches: Hq={heads[0]} Hkv={heads[1]} P={P}")
+        one = torch.empty_like(q)
+        ops.decode_fp8(one, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE),
+                       partition_size=P)
+        nb = ops.workspace_bytes(sp.num_seqs, sp.num_heads, sp.num_kv_heads, 128, 16,
+                                 case.max_blocks_per_seq, P)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        two = torch.empty_like(q)
+        ops.decode_fp8_partitions(two, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE),
+                                  float(V_SCALE), ws, partition_size=P)
+        ops.decode_merge(two, cl, sp.num_kv_heads, 16, case.max_blocks_per_seq, ws, partition_size=P)
+        torch.cuda.synchronize()
+        assert np.array_equal(W.from_torch(one, "bf16").view(np.uint16),
+                              W.from_torch(two, "bf16").view(np.uint16)), P

@@ -343,3 +343,27 @@ def test_prefill_gqa_full_size_sampled():
                                      np.array([0, 1], np.int32),
                                      np.array([n - L + i + 1], np.int32), bs, case.scale, "bf16")
             assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
+
+
+def test_plain_pa_prefill_entry():
+    """pa_prefill (no workspace, one pass over every key) called directly through the C ABI:
+    the same bits as pa_prefill_ex with a split length covering the table."""
+    import ctypes
+    import torch
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec("bf16", 16, 8, 2, (0, 300, 1000), (70, 1, 129), seed=26))
+    run = Prefill(case, dev)
+    sp = case.spec
+    maxb = case.pool.block_tables.shape[1]
+    ref = run.run(kv_split=(maxb * 16 + 63) // 64 * 64).copy()
+    lib = ops.load()
+    out = torch.empty_like(run.q)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.pa_prefill(ptr(out), ptr(run.q), ptr(run.kc), ptr(run.vc), ptr(run.bt), ptr(run.qsl),
+                        ptr(run.cl), sp.num_seqs, sp.num_heads, sp.num_kv_heads, 128, 16,
+                        case.pool.num_blocks, maxb, case.max_query_len, float(case.scale),
+                        ops._dtype_code(run.q), 0,
+                        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    assert st == 0, ops.status_string(st)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(W.from_torch(out, "bf16"), "bf16"), bits(ref, "bf16"))
