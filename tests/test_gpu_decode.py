@@ -30,18 +30,28 @@ def _mfma_ok(dtype, D, Hq, Hkv, P):
     return dtype in ("f16", "bf16") and D == 128 and (Hq // Hkv) % 4 == 0 and P % 16 == 0
 
 
-@pytest.mark.parametrize("partition", [0, 64, 48])
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("BS", [8, 16, 32])
-@pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def _decode_matrix():
+    """Every valid (dtype, head_dim, block size, kernel, partition) of the main sweep: a
+    partition is a multiple of the block size and of 16; the matrix-core kernel takes 16-bit
+    types, head_dim 128 and groups of 4k (8 query heads over 2 KV heads here)."""
+    cases = []
+    for dtype in ("f32", "f16", "bf16"):
+        for D in (64, 128):
+            for BS in (8, 16, 32):
+                for kernel in ("valu", "mfma"):
+                    for P in (0, 64, 48):
+                        if P % max(BS, 16):
+                            continue
+                        if kernel == "mfma" and not _mfma_ok(dtype, D, 8, 2, P or 512):
+                            continue
+                        cases.append((dtype, D, BS, kernel, P))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,D,BS,kernel,partition", _decode_matrix())
 def test_decode_matches_oracle(dtype, D, BS, kernel, partition):
     dev = need_gpu()
     Hq, Hkv = 8, 2
-    if partition % max(BS, 16):
-        pytest.skip("partition must be a multiple of the block size and of 16")
-    if kernel == "mfma" and not _mfma_ok(dtype, D, Hq, Hkv, partition or 512):
-        pytest.skip("matrix-core kernel needs f16/bf16, head_dim 128, groups of 4k")
     say(f"decode {dtype} D={D} BS={BS} kernel={kernel} P={partition}")
     c = _case(dtype, D, BS, Hq, Hkv, seed=zlib.crc32(f"{dtype}{D}{BS}".encode()) % 1000)
     u = Uploaded(c, dev)
@@ -50,15 +60,12 @@ def test_decode_matches_oracle(dtype, D, BS, kernel, partition):
     assert_attention_close(got, ref, dtype, live_vmax(c), f"{dtype}/{D}/{BS}/{kernel}/P{partition}")
 
 
-@pytest.mark.parametrize("BS", [64, 128])
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype,kernel,BS", [(d, k, b) for d in ("f32", "bf16") for k in ("valu", "mfma")
+                                              for b in (64, 128) if not (k == "mfma" and d == "f32")])
 def test_large_blocks(dtype, kernel, BS):
     """Block sizes 64 and 128 (several 16-token chunks per block), single pass and split."""
     dev = need_gpu()
     Hq, Hkv = 8, 2
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("matrix-core kernel needs f16/bf16")
     say(f"decode {dtype} BS={BS} kernel={kernel}")
     lengths = [1, BS - 1, BS, BS + 1, 3 * BS + 17, 700]
     c = _case(dtype, 128, BS, Hq, Hkv, lengths=lengths, seed=BS + len(dtype))
@@ -107,13 +114,14 @@ def test_head_dims_80_256(dtype, D, BS, heads):
                                f"D{D}/BS{BS}/G{Hq // Hkv}/P{P}")
 
 
-@pytest.mark.parametrize("heads", [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1)])
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+_GROUPINGS = [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1)]
+
+
+@pytest.mark.parametrize("heads,kernel", [(h, k) for h in _GROUPINGS for k in ("valu", "mfma")
+                                          if k == "valu" or _mfma_ok("bf16", 128, h[0], h[1], 64)])
 def test_head_groupings(heads, kernel):
     dev = need_gpu()
     Hq, Hkv = heads
-    if kernel == "mfma" and not _mfma_ok("bf16", 128, Hq, Hkv, 64):
-        pytest.skip("group not a multiple of 4")
     say(f"groups Hq={Hq} Hkv={Hkv} kernel={kernel}")
     c = _case("bf16", 128, 16, Hq, Hkv, lengths=[1, 17, 100, 333, 700], seed=7)
     u = Uploaded(c, dev)
@@ -134,13 +142,11 @@ def test_peaky_softmax(dtype, kernel):
                                f"peaky/{dtype}/{kernel}/P{P}")
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dtype,kernel", [(d, k) for d in ("f32", "f16", "bf16") for k in ("valu", "mfma")
+                                          if not (k == "mfma" and d == "f32")])
 def test_single_token_is_exact(dtype, kernel):
     """A one-token context returns that token's V bit for bit."""
     dev = need_gpu()
-    if kernel == "mfma" and dtype == "f32":
-        pytest.skip("no f32 matrix-core path")
     c = _case(dtype, 128, 16, 8, 2, lengths=[1] * 5, seed=12)
     got = Uploaded(c, dev).decode(kernel)
     ref = oracle_decode(c)
