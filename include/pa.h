@@ -1,6 +1,7 @@
 /*
- * pa.h — C ABI of libpa.so: paged decode attention and the two KV-cache kernels for
- * AMD MI355X (gfx950).
+ * pa.h — C ABI of libpa.so for AMD MI355X (gfx950): paged attention (single-query decode and
+ * chunked prefill) over a block-paged KV cache, the cache-writing and block-copy kernels
+ * (16-bit and 8-bit pools, swaps to and from host memory) and a block engine on the device.
  *
  * The problem, as the pages state it: the K/V cache of every sequence lives in fixed-size
  * blocks of one physical pool; a per-sequence block table maps logical blocks, in order, to
@@ -29,7 +30,11 @@
  *     streams) are safe.
  *
  * Element types: `pa_dtype` selects the element type of q, out, key, value and both pools
- * (all of one call share it).  Arithmetic is fp32 in every kernel.
+ * (all of one call share it).  Sums accumulate in fp32 in every kernel.  The vector-ALU decode
+ * kernels compute in fp32 throughout; the matrix-core kernels (grouped-query decode, prefill)
+ * multiply the 16-bit q, K and V as stored.  The grouped-query decode kernel multiplies the
+ * softmax probabilities as a 16-bit high part plus a 16-bit remainder (16 significant bits or
+ * more); pa_prefill states its own options.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -103,8 +108,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * num_kv_heads and KV head g = h / G (contiguous groups):
  *   K_t = key_cache[block_tables[s][t / block_size]][g][t % block_size][:]  (t < n), V alike
  *   z_t = scale * <query[s][h], K_t>
- *   out[s][h] = sum_t softmax(z)_t * V_t          (max-subtracted softmax, fp32 throughout)
- * and out[s][h] = 0 when n <= 0.  Paging changes where K/V live, not the result (the
+ *   out[s][h] = sum_t softmax(z)_t * V_t          (softmax evaluated stably, shifted by a
+ *                                                   running maximum; fp32 accumulation)
+ * and out[s][h] = 0 when n <= 0.  pa_decode runs the matrix-core kernel when dtype is
+ * PA_F16/PA_BF16, head_dim is 128 and G is a multiple of 4, and the vector-ALU kernel
+ * otherwise (arithmetic of each: see the element-type note at the top).  Paging changes where K/V live, not the result (the
  * xasun.com summary, section 一, calls the scheme lossless).
  *
  *   out           [num_seqs][num_heads][head_dim]                   dtype   (written)
