@@ -176,23 +176,29 @@ def test_fp8_block_copies():
     assert np.array_equal(host_k.numpy(), hk) and np.array_equal(host_v.numpy(), hv)
 
 
-def test_decode_fp8_full_size_sampled():
-    """The Llama-7B-shaped workload over an 8-bit cache (pools drawn on the GPU), run as the
-    benchmark runs it; six sequences checked against the oracle."""
+@pytest.mark.parametrize("name", ["llama7b_bs16_fp8", "gqa_long_fp8"])
+def test_decode_fp8_full_size_sampled(name):
+    """The Llama-7B-shaped (vector ALUs) and GQA long-context (matrix cores, 512-token
+    partitions) workloads over an 8-bit cache, pools drawn on the GPU, with the benchmark's
+    partition size; the longest, the shortest and four more sequences checked against the
+    oracle."""
     import torch
     dev = need_gpu()
-    spec = W.CONFIGS["llama7b_bs16_fp8"]
+    spec = W.CONFIGS[name]
     case = W.build_case(spec, device=dev)
-    say(f"decode_fp8 full size: {case.num_blocks} blocks")
+    say(f"decode_fp8 full size {name}: {case.num_blocks} blocks")
     q = W.to_torch(case.query, "bf16", dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
     cl = torch.from_numpy(case.context_lens).to(dev)
     out = torch.empty_like(q)
     ops.decode_fp8(out, q, case.key_cache, case.value_cache, bt, cl, float(case.scale),
-                   float(K_SCALE), float(V_SCALE))
+                   float(K_SCALE), float(V_SCALE), partition_size=spec.partition_size)
     torch.cuda.synchronize()
     got = W.from_torch(out, "bf16")
-    for s in (0, 1, 77, 128, 200, 255):
+    S = spec.num_seqs
+    order = np.argsort(case.context_lens)
+    picks = sorted({int(order[0]), int(order[-1]), 0, 1, S // 2, S - 1})
+    for s in picks:
         n = int(case.context_lens[s])
         nb = -(-n // 16)
         ids = torch.from_numpy(case.block_tables[s, :nb].astype(np.int64)).to(dev)
