@@ -134,6 +134,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int s = unit / (p.num_kv_heads * p.head_chunks);
   const int g = hc / p.head_chunks;
   const int h0 = g * p.group + (hc % p.head_chunks) * GT;
+  // Workgroups past a sequence's last partition leave before any vector load (as in the
+  // vector-ALU kernel); partition 0 always has work.
+  if (part > 0) {
+    const int n0 = min(p.context_lens[s], p.max_blocks_per_seq * BS);
+    if (part * p.partition >= n0) return;
+  }
 
   // Loads independent of the context length first (their latency overlaps the read of
   // context_lens): the Q^T operand and the table entries of this wave's first 64 chunks
@@ -330,23 +336,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
         okm = (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
       }
     };
-    // Two register buffers, steady-state loads unconditional (see the vector-ALU kernel).
+    // Two register buffers, steady-state loads unconditional (see the vector-ALU kernel).  A
+    // scheduling barrier after each chunk's load issue keeps the intended order: without it
+    // the compiler moved the next chunk's LDS stores of K -- and the wait for its K loads that
+    // they need -- above the current chunk's products, so the chunk after next was issued only
+    // once the next one had arrived (about 1.5 chunks in flight instead of 2).
     Chunk ca, cb;
     int oka, okb;
     phys_of(0, oka);
     load_chunk(ca, ph0, ph1, base);
+    __builtin_amdgcn_sched_barrier(0);
     int i = 0;
     for (; i + 2 < cnt; i += 2) {
       phys_of(i + 1, okb);
       load_chunk(cb, ph0, ph1, base + 4 * (i + 1));
+      __builtin_amdgcn_sched_barrier(0);
       consume(ca, base + 4 * i, oka);
       phys_of(i + 2, oka);
       load_chunk(ca, ph0, ph1, base + 4 * (i + 2));
+      __builtin_amdgcn_sched_barrier(0);
       consume(cb, base + 4 * (i + 1), okb);
     }
     if (i + 1 < cnt) {
       phys_of(i + 1, okb);
       load_chunk(cb, ph0, ph1, base + 4 * (i + 1));
+      __builtin_amdgcn_sched_barrier(0);
       consume(ca, base + 4 * i, oka);
       consume(cb, base + 4 * (i + 1), okb);
     } else {

@@ -85,6 +85,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int s = r / p.num_kv_heads;
   const int g = r - s * p.num_kv_heads;
   const int h0 = g * p.group + chunk * GT;
+  // The grid holds every partition a full table could need, so workgroups past a sequence's
+  // last partition are common (tables sized for long contexts, short sequences).  Such a
+  // workgroup reads the length alone and leaves before issuing any vector load: with the
+  // query and table loads below in flight it would have to wait for them before ending.
+  // Partition 0 always has work, so it skips this check and keeps the early loads.
+  if (part > 0) {
+    const int n0 = min(p.context_lens[s], p.max_blocks_per_seq * BS);
+    if (part * p.partition >= n0) return;
+  }
 
   // Loads that do not depend on the context length go first, so their latency overlaps the
   // read of context_lens: the query rows and the table entries of this wave's first chunks
