@@ -241,6 +241,30 @@ def test_very_long_context(kernel):
         assert_attention_close(u.decode(kernel, P), ref, "bf16", live_vmax(c), f"long/{kernel}/P{P}")
 
 
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_wide_tables_short_contexts(kernel):
+    """Tables sized for far longer contexts than the batch holds (4096 entries, 64K tokens) with
+    small partitions: almost every workgroup of the grid lies past its sequence's last partition
+    and leaves at once.  With a given partition size: same bits as the tight tables; every run
+    within the bar of the oracle (the library's own choice, P = 0, depends on the table width)."""
+    import torch
+    dev = need_gpu()
+    c = _case("bf16", 128, 16, 8, 2, lengths=[1, 16, 17, 300, 64, 1000], seed=23)
+    tight = Uploaded(c, dev)
+    wide = Uploaded(c, dev)
+    padded = np.full((len(c.context_lens), 4096), -1, np.int32)
+    padded[:, :c.block_tables.shape[1]] = c.block_tables
+    wide.bt = torch.from_numpy(padded).to(dev)
+    ref = oracle_decode(c)
+    for P in (64, 512, 0):
+        say(f"decode {kernel} wide tables P={P}")
+        a = tight.decode(kernel, P)
+        b = wide.decode(kernel, P)
+        if P:
+            assert np.array_equal(bits(a, "bf16"), bits(b, "bf16")), P
+        assert_attention_close(b, ref, "bf16", live_vmax(c), f"wide/{kernel}/P{P}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.0883883, -2.0])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 def test_zero_and_negative_scale(kernel, scale):
