@@ -175,6 +175,7 @@ def time_steps(step, steps, warmup):
 
 
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache
+COLD_WORKLOADS = ("tiny", "gqa_long", "shared_prefix")
 
 
 def time_steps_cold(step, steps):
@@ -201,16 +202,28 @@ def time_steps_cold(step, steps):
 
 
 def snapshot_sequences(case, seqs):
-    """Host copies of the blocks the given sequences read (taken before any step runs)."""
+    """Host copies of the blocks each given sequence reads in the step (with the copy-on-write
+    sources of its blocks), renumbered 0.., taken before any step runs."""
     import torch
     bs = case.block_size
+    pdt = case.spec.kv_dtype or case.dtype
+    pairs_all = np.asarray(case.block_mapping).reshape(-1, 2)
+    own_slot = case.spec.new_tokens == "next" and len(case.slot_mapping) == case.spec.num_seqs
     out = []
     for s in seqs:
         n = int(case.context_lens[s])
-        row = case.block_tables[s, : -(-n // bs)].astype(np.int64)
-        idx = torch.from_numpy(row).to(case.key_cache.device)
-        out.append((s, n, W.from_torch(case.key_cache.index_select(0, idx), case.dtype),
-                    W.from_torch(case.value_cache.index_select(0, idx), case.dtype)))
+        row = [int(b) for b in case.block_tables[s, : -(-n // bs)]]
+        pairs = [(int(a), int(b)) for a, b in pairs_all if int(b) in row]
+        blocks = sorted(set(row) | {a for a, _ in pairs})
+        remap = {b: i for i, b in enumerate(blocks)}
+        idx = torch.tensor(blocks, dtype=torch.int64, device=case.key_cache.device)
+        slot = int(case.slot_mapping[s]) if own_slot else -1
+        out.append(dict(
+            s=s, n=n, table=np.array([[remap[b] for b in row]], np.int32),
+            pairs=np.array([[remap[a], remap[b]] for a, b in pairs], np.int64).reshape(-1, 2),
+            slot=np.array([remap[slot // bs] * bs + slot % bs] if slot >= 0 else [], np.int64),
+            mk=W.from_torch(case.key_cache.index_select(0, idx), pdt),
+            mv=W.from_torch(case.value_cache.index_select(0, idx), pdt)))
     return out
 
 
@@ -222,40 +235,93 @@ def host_threads() -> int:
         return max(1, min(16, os.cpu_count() or 1))
 
 
-def cpu_baseline(case, snaps, budget_s, threads=1):
-    """The float64 oracle decoding the snapshotted sequences one at a time (BLAS limited to
-    ``threads`` threads), cycling over them until at least one full pass and ``budget_s``
-    seconds are done."""
+def oracle_inputs(case, snaps):
+    """Per snapshotted sequence, the pools the decode reads: the step's copy-on-write pairs and
+    its new token applied by the oracle (untimed), with the sequence's renumbered table."""
+    import oracle
+    bs = case.block_size
+    fp8 = case.spec.kv_dtype == "fp8"
+    prepared = []
+    for sn in snaps:
+        mk, mv = sn["mk"], sn["mv"]
+        s = sn["s"]
+        if len(sn["pairs"]):
+            mk, mv = oracle.copy_blocks_ref(mk, mv, sn["pairs"])
+        if len(sn["slot"]):
+            if fp8:
+                mk, mv = oracle.reshape_and_cache_fp8_ref(
+                    case.new_key[s:s + 1], case.new_value[s:s + 1], mk, mv, sn["slot"], bs,
+                    case.dtype, W.FP8_DRAW_SCALE, W.FP8_DRAW_SCALE)
+            else:
+                mk, mv = oracle.reshape_and_cache_ref(case.new_key[s:s + 1], case.new_value[s:s + 1],
+                                                      mk, mv, sn["slot"], bs)
+        prepared.append((s, sn["n"], mk, mv, sn["table"]))
+    return prepared
+
+
+def cpu_baseline(case, prepared, budget_s, threads=1):
+    """The float64 oracle decoding the prepared sequences, one decode_ref call per sequence,
+    ``threads`` of them at a time in a thread pool (numpy releases the interpreter lock inside
+    its array loops and BLAS calls; BLAS itself is held to one thread per worker).  Sequences
+    are taken in order, cycling, until at least ``budget_s`` wall seconds and one decode per
+    worker are done.  Rates are per wall second."""
+    import concurrent.futures as cf
     import oracle
     from threadpoolctl import threadpool_limits
     sp = case.spec
-    bs = case.block_size
     e = W.ELEM_BYTES[sp.dtype]
-    prepared = []
-    for s, n, mk, mv in snaps:
-        table = np.arange(mk.shape[0], dtype=np.int32)[None]
-        slot = np.array([n - 1], np.int64)   # the new token: last slot of the sequence
-        mk, mv = oracle.reshape_and_cache_ref(case.new_key[s:s + 1], case.new_value[s:s + 1],
-                                              mk, mv, slot, bs)   # the step's write (untimed)
-        prepared.append((s, n, mk, mv, table))
-    done, bytes_done, heads, tokens, elapsed = 0, 0, 0, 0, 0.0
-    with threadpool_limits(limits=threads):
-        while done < len(prepared) or elapsed < budget_s:
-            s, n, mk, mv, table = prepared[done % len(prepared)]
-            t = time.perf_counter()
+    ekv = W.ELEM_BYTES[sp.kv_dtype or sp.dtype]
+    fp8 = sp.kv_dtype == "fp8"
+    bs = case.block_size
+
+    def one(item):
+        s, n, mk, mv, table = item
+        if fp8:
+            oracle.decode_fp8_ref(case.query[s:s + 1], mk, mv, table, np.array([n], np.int32), bs,
+                                  case.scale, case.dtype, W.FP8_DRAW_SCALE, W.FP8_DRAW_SCALE)
+        else:
             oracle.decode_ref(case.query[s:s + 1], mk, mv, table, np.array([n], np.int32), bs,
                               case.scale, case.dtype)
-            elapsed += time.perf_counter() - t
-            bytes_done += n * sp.num_kv_heads * sp.head_dim * e * 2 + sp.num_heads * sp.head_dim * e * 2
-            heads += sp.num_heads
-            tokens += n
-            done += 1
-    return {"value": round(bytes_done / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+        return n
+
+    done, tokens = 0, 0
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        while True:
+            batch = [prepared[(done + k) % len(prepared)] for k in range(threads)]
+            for n in ex.map(one, batch):
+                tokens += n
+            done += len(batch)
+            elapsed = time.perf_counter() - t0
+            if elapsed >= budget_s:
+                break
+    nbytes = tokens * sp.num_kv_heads * sp.head_dim * ekv * 2 + done * sp.num_heads * sp.head_dim * e * 2
+    heads = done * sp.num_heads
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seq_heads_per_s": round(heads / elapsed, 2),
+            "s_per_call": float(f"{elapsed * sp.num_seqs / done:.4g}"),
             "seconds": round(elapsed, 2),
-            "sample": f"{done} sequence decodes cycling over the {len(prepared)} sequences of the "
-                      f"step ({tokens} cached tokens read, all {sp.num_heads} heads each), numpy "
-                      f"float64, {threads} BLAS thread{'s' if threads > 1 else ''}"}
+            "sample": f"{done} sequence decodes taken in order, cycling over the {len(prepared)} "
+                      f"sequences of the step ({tokens} cached tokens read, all {sp.num_heads} "
+                      f"heads each), numpy float64, {threads} worker thread"
+                      f"{'s' if threads > 1 else ''} with one BLAS thread each"}
+
+
+# CPU-baseline legs: one per workload family, the one-thread leg where it is asked for
+CPU_BASELINE_LEGS = {"tiny": False, "opt13b": True, "llama7b_bs16": True, "gqa_long": False,
+                     "shared_prefix": False}
+
+
+def cpu_baseline_leg(case, snaps, budget_s, one_thread):
+    """The oracle on the host's cores, and on one thread when ``one_thread``."""
+    prepared = oracle_inputs(case, snaps)
+    nt = host_threads()
+    rec = cpu_baseline(case, prepared, budget_s, nt)
+    if one_thread and nt > 1:
+        one = cpu_baseline(case, prepared, budget_s, 1)
+        rec["one_thread"] = {k: one[k] for k in ("value", "seq_heads_per_s", "s_per_call", "seconds")}
+        rec["speedup_vs_one_thread"] = round(rec["value"] / one["value"], 2)
+    return rec
 
 
 def traffic_for(kernel, workload):
@@ -290,6 +356,38 @@ def copy_ceiling(dev, steps):
     moved = 2 * (nb // 2) * 32 * 16 * 128 * 2
     del kc, vc
     return ms, moved
+
+
+def read_ceiling(dev, steps):
+    """pa_read_tiles over a 2 GiB buffer of 4 KiB tiles (one (block, KV head) tile of the
+    16-token bf16 workloads): the tiles as one contiguous run, then the same tiles in a seeded
+    random order (the decode's pattern: whole tiles scattered over the pool).  Nothing but the
+    loads and an XOR per tile, so these are the read rates a decode kernel could reach."""
+    import torch
+    nbytes, tile = 2 << 30, 4096
+    ntiles = nbytes // tile
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    out = torch.empty(ntiles, dtype=torch.int32, device=dev)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(4096)
+    ids = torch.randperm(ntiles, generator=g).to(torch.int32).to(dev)
+    res = {"what": "pa_read_tiles, 2 GiB of 4 KiB tiles read per launch (16-byte non-temporal loads)"}
+    for name, tid in (("contiguous", None), ("scattered_tiles", ids)):
+        for _ in range(3):
+            ops.read_tiles(buf, tile, out, tid)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            ops.read_tiles(buf, tile, out, tid)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        res[name] = {"ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
+                     "frac_of_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del buf, out, ids
+    return res
 
 
 def calibrate_copy(dev, steps):
@@ -459,10 +557,13 @@ def measure_device_engine(dev, steps, warmup):
             "sequences": S}
 
 
-def run_workload(name, dev, steps, warmup, kernel):
+def run_workload(name, dev, steps, warmup, kernel, snap=False):
+    """Build the workload on the GPU and time its steps.  With ``snap`` the blocks every
+    sequence reads are copied to the host first (for the CPU baseline); returned as case.snaps."""
     import torch
     case = W.build_case(W.CONFIGS[name], device=dev)
     torch.cuda.synchronize()
+    case.snaps = snapshot_sequences(case, range(case.spec.num_seqs)) if snap else None
     step = Step(case, dev, kernel)
     ms, kern_ms, kern_min, wall = time_steps(step, steps, warmup)
     return case, step, ms, kern_ms, kern_min, wall
@@ -477,7 +578,8 @@ def main(argv=None):
     ap.add_argument("--also", default="llama7b_bs32,llama7b_bs8,opt13b,gqa_long,shared_prefix,llama7b_bs16_fp8,gqa_long_fp8,tiny",
                     help="comma-separated extra workloads timed for the detail field ('' for none)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="wall seconds of each CPU-baseline leg (per workload and thread count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--only", default="",
@@ -529,13 +631,10 @@ def main(argv=None):
         return 0
 
     name = args.workload
-    case = W.build_case(W.CONFIGS[name], device=dev)
-    torch.cuda.synchronize()
-    snaps = None
-    if not args.no_cpu_baseline:
-        snaps = snapshot_sequences(case, range(case.spec.num_seqs))
-    step = Step(case, dev, args.kernel)
-    ms, kern_ms, kern_min, wall = time_steps(step, args.steps, args.warmup)
+    want_cpu = lambda w: not args.no_cpu_baseline and w in CPU_BASELINE_LEGS
+    cpu_legs = {}
+    case, step, ms, kern_ms, kern_min, wall = run_workload(name, dev, args.steps, args.warmup,
+                                                           args.kernel, snap=want_cpu(name))
     sp = case.spec
     dbytes = decode_bytes(case)
     sbytes = dbytes + cache_write_bytes(case)
@@ -576,11 +675,15 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": dbytes,
         },
     }
+    if case.snaps is not None:
+        cpu_legs[name] = cpu_baseline_leg(case, case.snaps, args.cpu_seconds, CPU_BASELINE_LEGS[name])
+        case.snaps = None
     detail = {}
     for extra in [x for x in args.also.split(",") if x and x != name]:
         del step
         torch.cuda.empty_cache()
-        c2, step, ms2, k2, k2min, _ = run_workload(extra, dev, args.steps, args.warmup, args.kernel)
+        c2, step, ms2, k2, k2min, _ = run_workload(extra, dev, args.steps, args.warmup, args.kernel,
+                                                   snap=want_cpu(extra))
         b2 = decode_bytes(c2)
         detail[extra] = {"ms_per_step": round(ms2, 4),
                          "GBps_step": round((b2 + cache_write_bytes(c2)) / (ms2 * 1e-3) / 1e9, 2),
@@ -593,11 +696,16 @@ def main(argv=None):
         if c2.spec.shared_prefix:
             detail[extra]["unique_kv_bytes"] = ub
             detail[extra]["decode_kernel_unique_GBps"] = round(ub / (k2 * 1e-3) / 1e9, 2)
-        if ub < 4 * MALL_BYTES:   # fits the caches: also report cold-cache steps
+        # workloads that fit the caches, and the small-batch ones (tiny, GQA long, shared
+        # prefix), are also timed with cold caches
+        if ub < 4 * MALL_BYTES or extra in COLD_WORKLOADS:
             cms, ck = time_steps_cold(step, args.steps)
             detail[extra]["cold"] = {"ms_per_step": round(cms, 4), "decode_kernel_ms": round(ck, 4),
                                      "decode_kernel_GBps": round(b2 / (ck * 1e-3) / 1e9, 2),
                                      "note": "median; 1 GiB written before each step"}
+        if c2.snaps is not None:
+            cpu_legs[extra] = cpu_baseline_leg(c2, c2.snaps, args.cpu_seconds, CPU_BASELINE_LEGS[extra])
+            c2.snaps = None
         del c2
     if detail:
         del step
@@ -609,18 +717,19 @@ def main(argv=None):
                                   "ms": round(cms, 4),
                                   "GBps_read_plus_write": round(2 * cmoved / cms / 1e6, 1)}
         torch.cuda.empty_cache()
+        detail["read_ceiling"] = read_ceiling(dev, max(5, args.steps // 2))
+        torch.cuda.empty_cache()
         for pname in ("prefill_llama7b", "prefill_gqa"):
             detail[pname] = measure_prefill(dev, pname, args.steps, args.warmup)
         torch.cuda.empty_cache()
         detail["shared_prefix_device_engine"] = measure_device_engine(dev, args.steps, args.warmup)
         rec["detail"] = detail
-    if snaps is not None:
-        # the host's cores (BLAS threads), plus a one-thread timing for context
-        nt = host_threads()
-        rec["cpu_baseline"] = cpu_baseline(case, snaps, 0.6 * args.cpu_seconds, nt)
-        if nt > 1:
-            one = cpu_baseline(case, snaps, 0.4 * args.cpu_seconds, 1)
-            rec["cpu_baseline"]["one_thread"] = {k: one[k] for k in ("value", "seq_heads_per_s", "seconds")}
+    if cpu_legs:
+        # the headline workload's leg on top, every workload's leg under per_config
+        head = cpu_legs.get(name) or next(iter(cpu_legs.values()))
+        rec["cpu_baseline"] = dict(head)
+        rec["cpu_baseline"]["workload"] = name if name in cpu_legs else next(iter(cpu_legs))
+        rec["cpu_baseline"]["per_config"] = cpu_legs
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -441,6 +441,22 @@ pa_status pa_block_hashes(const int32_t* token_ids, const int32_t* num_tokens, i
                           int32_t max_tokens, int32_t block_size, uint64_t* hashes,
                           void* stream);
 
+/*
+ * pa_read_tiles — read-only bandwidth probe (measurement, not part of the attention path).
+ * Decode is bound by memory bandwidth (xasun.com summary §三, compute-pattern row), so its
+ * achieved rate is compared with what a kernel that only reads can reach in the same access
+ * pattern.  The buffer `base` holds base_tiles tiles of tile_bytes bytes each; tile t of the
+ * call is tile tile_ids[t] of the buffer (tile_ids NULL: tile t itself, a contiguous run).
+ * Every tile is read whole with the decode kernels' loads (16 bytes per lane, non-temporal)
+ * and xor_out[t] (uint32, device, num_tiles entries, written) receives the XOR of its 32-bit
+ * words; a tile id outside [0, base_tiles) is skipped and reports 0.
+ * Supported: tile_bytes 1024, 2048, 4096 or 8192; with tile_ids NULL, num_tiles <= base_tiles.
+ * Errors: PA_ERR_NULL_PTR, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH.
+ */
+pa_status pa_read_tiles(const void* base, int64_t base_tiles, int32_t tile_bytes,
+                        const int32_t* tile_ids, int32_t num_tiles, uint32_t* xor_out,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

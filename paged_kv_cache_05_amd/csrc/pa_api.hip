@@ -66,6 +66,7 @@ pa_status check_shape(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
 int auto_partition(int32_t S, int32_t Hkv, int32_t BS, int32_t maxb) {
   const long cap = (long)maxb * BS;
   const long units = (long)S * Hkv;
+  if (units <= 0) return 0;   // an empty batch: nothing to split
   const long parts = std::max(1L, (kTargetWorkgroups + units - 1) / units);
   long P = (cap + parts - 1) / parts;
   P = std::min<long>(std::max<long>(P, kMinPartition), kMaxPartition);
@@ -689,6 +690,20 @@ pa_status pa_copy_blocks_counted(void* key_cache, void* value_cache, const int64
                                              block_mapping, max_pairs, block_bytes / 16,
                                              num_blocks, num_blocks,
                                              reinterpret_cast<hipStream_t>(stream), num_pairs));
+}
+
+pa_status pa_read_tiles(const void* base, int64_t base_tiles, int32_t tile_bytes,
+                        const int32_t* tile_ids, int32_t num_tiles, uint32_t* xor_out,
+                        void* stream) {
+  if (num_tiles < 0 || base_tiles <= 0) return PA_ERR_BAD_SHAPE;
+  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192)
+    return PA_ERR_UNSUPPORTED;
+  if (!tile_ids && num_tiles > base_tiles) return PA_ERR_BAD_SHAPE;   // contiguous run past the buffer
+  if (num_tiles == 0) return PA_OK;
+  if (!base || !xor_out) return PA_ERR_NULL_PTR;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_read_tiles(base, (long)base_tiles, tile_bytes, tile_ids, num_tiles,
+                                             xor_out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_block_hashes(const int32_t* token_ids, const int32_t* num_tokens, int32_t num_seqs,

@@ -291,6 +291,11 @@ hipError_t launch_block_copy(const void* src_k, const void* src_v, void* dst_k, 
                              int src_blocks, int dst_blocks, hipStream_t st,
                              const int32_t* count = nullptr);
 
+// read-only bandwidth probe (pa_read_tiles); ids may be null (tile t is tile t)
+hipError_t launch_read_tiles(const void* base, long base_tiles, int tile_bytes,
+                             const int32_t* ids, int num_tiles, uint32_t* xor_out,
+                             hipStream_t st);
+
 struct EngineState {           // block-engine state kept on the device (all caller-owned)
   int32_t* tables;             // [num_seqs][max_blocks_per_seq]
   int32_t* context_lens;       // [num_seqs]

@@ -60,6 +60,7 @@ _SIGNATURES = {
     "pa_decode_fp8_partitions": (_c_int, [_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_float,
                                                                  _c_float, _c_int, _p, _c_size,
                                                                  ctypes.c_uint32, _p]),
+    "pa_read_tiles": (_c_int, [_p, ctypes.c_int64, _c_int, _p, _c_int, _p, _p]),
 }
 
 
@@ -70,9 +71,16 @@ def header_symbols() -> list[str]:
 
 
 def load():
-    """Load libpa.so (once); raises if it has not been built."""
+    """Load libpa.so (once); raises if it has not been built.
+
+    torch is imported first: it loads its own copy of the HIP runtime, whose soname
+    (libamdhip64.so.7) is the one libpa.so links against, so the library binds to that copy.
+    Loaded before torch, libpa.so would pull in the system copy as well, and its calls would go
+    to a second runtime that does not see torch's device state (its hipGetDevice reports no
+    device)."""
     global _lib
     if _lib is None:
+        import torch  # noqa: F401
         if not LIB_PATH.exists():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "paged_kv_cache_05_amd.build.build() (hipcc, gfx950)")
@@ -481,3 +489,26 @@ def block_hashes(token_ids, num_tokens, block_size, hashes, *, stream=None):
         raise ValueError("hashes must be 64-bit [num_seqs, max_tokens // block_size]")
     _check(load().pa_block_hashes(_ptr(token_ids), _ptr(num_tokens), S, T, int(block_size),
                                   _ptr(hashes), _stream(dev, stream)), "pa_block_hashes")
+
+
+# ---------------------------------------------------------------------------------------
+# read-only bandwidth probe
+# ---------------------------------------------------------------------------------------
+def read_tiles(buffer, tile_bytes, xor_out, tile_ids=None, *, stream=None):
+    """pa_read_tiles: read tiles of ``tile_bytes`` bytes of ``buffer`` (any contiguous GPU
+    tensor) -- tile t is tile ``tile_ids[t]`` (int32), or tile t itself when ``tile_ids`` is
+    None -- and write the XOR of each tile's 32-bit words to ``xor_out`` (32-bit, one entry per
+    tile read)."""
+    import torch
+    dev = _dev(buffer, xor_out, tile_ids)
+    nbytes = buffer.numel() * buffer.element_size()
+    if xor_out.element_size() != 4:
+        raise TypeError("xor_out must hold 32-bit words")
+    n = tile_ids.numel() if tile_ids is not None else xor_out.numel()
+    if tile_ids is not None and tile_ids.dtype != torch.int32:
+        raise TypeError("tile_ids must be int32")
+    if xor_out.numel() < n:
+        raise ValueError("xor_out needs one entry per tile read")
+    _check(load().pa_read_tiles(_ptr(buffer), nbytes // int(tile_bytes), int(tile_bytes),
+                                _ptr(tile_ids), n, _ptr(xor_out), _stream(dev, stream)),
+           "pa_read_tiles")

@@ -127,3 +127,83 @@ def assert_attention_close(gpu_storage, ref64, dtype, vmax, what=""):
 def bits(storage, dtype):
     a = np.ascontiguousarray(storage)
     return a.view(np.uint32) if dtype == "f32" else a.view(np.uint16)
+
+
+# ---------------------------------------------------------------------------------------
+# full-size parity: every sequence of a GPU-drawn workload against the oracle
+# ---------------------------------------------------------------------------------------
+def host_threads() -> int:
+    """Host cores this process may use (its affinity mask), at most 16 (one GPU's share)."""
+    import os
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def snapshot_seq(case: W.DecodeCase, s: int, kc, vc, pool_dtype=None) -> dict:
+    """Host copies of every block sequence s reads in this step (and the copy-on-write sources
+    of its blocks), renumbered 0.., with the step's table row, copy pairs and slot in that
+    numbering.  Taken from the GPU pools ``kc``/``vc``."""
+    import torch
+    pdt = pool_dtype or case.dtype
+    bs = case.block_size
+    n = int(case.context_lens[s])
+    nb = -(-n // bs)
+    row = [int(b) for b in case.block_tables[s, :nb]]
+    pairs = [(int(a), int(b)) for a, b in np.asarray(case.block_mapping).reshape(-1, 2) if int(b) in row]
+    blocks = sorted(set(row) | {a for a, _ in pairs})
+    remap = {b: i for i, b in enumerate(blocks)}
+    idx = torch.tensor(blocks, dtype=torch.int64, device=kc.device)
+    mk = W.from_torch(kc.index_select(0, idx), pdt)
+    mv = W.from_torch(vc.index_select(0, idx), pdt)
+    table = np.array([[remap[b] for b in row]], dtype=np.int32)
+    mpairs = np.array([[remap[a], remap[b]] for a, b in pairs], dtype=np.int64).reshape(-1, 2)
+    # with one appended token per sequence, slot_mapping[s] is sequence s's new token
+    own = case.spec.new_tokens == "next" and len(case.slot_mapping) == case.spec.num_seqs
+    slot = int(case.slot_mapping[s]) if own else -1
+    mslot = np.array([remap[slot // bs] * bs + slot % bs], dtype=np.int64) if slot >= 0 else \
+        np.zeros(0, np.int64)
+    return dict(s=s, blocks=blocks, mk=mk, mv=mv, table=table, pairs=mpairs, slot=mslot, n=n)
+
+
+def compare_every_sequence(case: W.DecodeCase, got, kc, vc, snaps, oracle_seq, what,
+                           pool_dtype=None, batch=32):
+    """The whole GPU output ``got`` ([S, Hq, d] storage) against the oracle, sequence by
+    sequence (``oracle_seq(snap) -> (out [Hq, d] float64, pool_k, pool_v, max|V| of the
+    sequence)``, run in a thread pool), checked at the attention bar over the whole tensor;
+    and, for every sequence, the blocks it reads after the step bit for bit against the
+    oracle's pools (every block the step wrote is among them)."""
+    import concurrent.futures as cf
+    import torch
+    from threadpoolctl import threadpool_limits
+    pdt = pool_dtype or case.dtype
+    S = case.spec.num_seqs
+    ref = np.zeros(got.shape, dtype=np.float64)
+    vmax = 0.0
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        for b0 in range(0, S, batch):
+            seqs = range(b0, min(S, b0 + batch))
+            futs = {s: ex.submit(oracle_seq, snaps[s]) for s in seqs}
+            after = {}
+            for s in seqs:      # the GPU pools after the step, the same blocks
+                idx = torch.tensor(snaps[s]["blocks"], dtype=torch.int64, device=kc.device)
+                after[s] = (W.from_torch(kc.index_select(0, idx), pdt),
+                            W.from_torch(vc.index_select(0, idx), pdt))
+            for s in seqs:
+                out_s, rk, rv, vm = futs[s].result()
+                ref[s] = out_s
+                vmax = max(vmax, vm)
+                ak, av = after[s]
+                assert np.array_equal(ak.view(np.uint8), np.ascontiguousarray(rk).view(np.uint8)), \
+                    f"{what}: key blocks of sequence {s} differ from the oracle's"
+                assert np.array_equal(av.view(np.uint8), np.ascontiguousarray(rv).view(np.uint8)), \
+                    f"{what}: value blocks of sequence {s} differ from the oracle's"
+            del futs, after
+    out_dt = case.dtype
+    worst = max(range(S), key=lambda s: float(np.max(np.abs(
+        oracle.storage_to_f64(got[s], out_dt) -
+        oracle.storage_to_f64(oracle.f64_to_storage(ref[s], out_dt), out_dt)))))
+    say(f"  {what}: {S} sequences compared; largest error in sequence {worst} "
+        f"(n={int(case.context_lens[worst])})")
+    return assert_attention_close(got, ref, out_dt, vmax, f"{what} (all {S} sequences)")

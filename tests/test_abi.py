@@ -250,3 +250,41 @@ def test_block_engine_argument_errors(lib):
     assert h(p, p, 4, 64, 0, p, None) == 2
     assert h(p, None, 4, 64, 16, p, None) == 1
     assert h(None, None, 4, 8, 16, None, None) == 0                            # no full block
+
+
+def test_read_tiles_argument_errors(lib):
+    p = lambda v: ctypes.c_void_p(v) if v else None
+    f = lib.pa_read_tiles
+    assert f(p(1), 10, 4096, None, 4, None, None) == 1          # PA_ERR_NULL_PTR
+    assert f(None, 10, 4096, None, 4, p(1), None) == 1
+    assert f(p(1), 10, 4096, None, -1, p(1), None) == 2         # PA_ERR_BAD_SHAPE
+    assert f(p(1), 0, 4096, None, 4, p(1), None) == 2
+    assert f(p(1), 10, 4096, None, 11, p(1), None) == 2         # contiguous run past the buffer
+    assert f(p(1), 10, 4096, p(1), 11, None, None) == 1         # scattered ids may repeat tiles
+    assert f(p(1), 10, 3000, None, 4, p(1), None) == 3          # PA_ERR_UNSUPPORTED tile size
+    assert f(p(1), 10, 16384, None, 4, p(1), None) == 3
+    assert f(None, 10, 4096, None, 0, None, None) == 0          # nothing to read: no-op
+
+
+def test_empty_batch_sizes(lib):
+    """An empty batch needs no workspace and no split (no division by the unit count)."""
+    assert lib.pa_decode_workspace_bytes(0, 32, 32, 128, 16, 64, 0) == 0
+    assert lib.pa_decode_auto_partition(0, 32, 8, 128, 16, 64) >= 64 * 16   # one pass
+    assert lib.pa_decode_workspace_bytes(0, 32, 32, 128, 16, 64, 256) == 0
+
+
+def test_one_hip_runtime_per_process(lib):
+    """libpa.so binds to torch's copy of the HIP runtime even when the binding is loaded before
+    anything imports torch: a second copy would take the library's calls to a runtime that has
+    none of torch's device state."""
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from paged_kv_cache_05_amd import ops\n"
+            "ops.load()\n"
+            "import torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n"
+            % str(ops.LIB_PATH.parents[1]))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         timeout=300).stdout
+    mapped = eval(out.strip().splitlines()[-1])
+    assert len(mapped) == 1, mapped

@@ -12,7 +12,7 @@ import oracle
 from paged_kv_cache_05_amd import ops
 from paged_kv_cache_05_amd import workloads as W
 
-from gpu_helpers import assert_attention_close, need_gpu, say
+from gpu_helpers import assert_attention_close, compare_every_sequence, need_gpu, say, snapshot_seq
 
 pytestmark = pytest.mark.gpu
 
@@ -177,37 +177,48 @@ def test_fp8_block_copies():
 
 
 @pytest.mark.parametrize("name", ["llama7b_bs16_fp8", "gqa_long_fp8"])
-def test_decode_fp8_full_size_sampled(name):
+def test_decode_fp8_full_size_every_sequence(name):
     """The Llama-7B-shaped (vector ALUs) and GQA long-context (matrix cores, 512-token
-    partitions) workloads over an 8-bit cache, pools drawn on the GPU, with the benchmark's
-    partition size; the longest, the shortest and four more sequences checked against the
-    oracle."""
+    partitions) steps over an 8-bit cache, pools drawn on the GPU, in the benchmark's launch
+    configuration: reshape_and_cache_fp8 of each sequence's new token, then pa_decode_fp8.
+    Every sequence is checked against the oracle chain (quantise -> store -> dequantise ->
+    attend), the whole output at the attention bar, and every block a sequence reads after the
+    step (its new token's block among them) bit for bit."""
     import torch
     dev = need_gpu()
     spec = W.CONFIGS[name]
     case = W.build_case(spec, device=dev)
     say(f"decode_fp8 full size {name}: {case.num_blocks} blocks")
+    kc, vc = case.key_cache, case.value_cache
+    snaps = [snapshot_seq(case, s, kc, vc, pool_dtype="fp8") for s in range(spec.num_seqs)]
     q = W.to_torch(case.query, "bf16", dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
     cl = torch.from_numpy(case.context_lens).to(dev)
     out = torch.empty_like(q)
-    ops.decode_fp8(out, q, case.key_cache, case.value_cache, bt, cl, float(case.scale),
-                   float(K_SCALE), float(V_SCALE), partition_size=spec.partition_size)
+    ops.reshape_and_cache_fp8(W.to_torch(case.new_key, "bf16", dev),
+                              W.to_torch(case.new_value, "bf16", dev), kc, vc,
+                              torch.from_numpy(case.slot_mapping).to(dev), float(K_SCALE),
+                              float(V_SCALE))
+    ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE),
+                   partition_size=spec.partition_size)
     torch.cuda.synchronize()
-    got = W.from_torch(out, "bf16")
-    S = spec.num_seqs
-    order = np.argsort(case.context_lens)
-    picks = sorted({int(order[0]), int(order[-1]), 0, 1, S // 2, S - 1})
-    for s in picks:
-        n = int(case.context_lens[s])
-        nb = -(-n // 16)
-        ids = torch.from_numpy(case.block_tables[s, :nb].astype(np.int64)).to(dev)
-        kc = W.from_torch(case.key_cache.index_select(0, ids), "fp8")
-        vc = W.from_torch(case.value_cache.index_select(0, ids), "fp8")
-        ref = oracle.decode_fp8_ref(case.query[s:s + 1], kc, vc, np.arange(nb, dtype=np.int32)[None],
-                                    np.array([n], np.int32), 16, case.scale, "bf16", K_SCALE, V_SCALE)
-        vmax = float(np.max(np.abs(oracle.dequantize_fp8(vc, V_SCALE))))
-        assert_attention_close(got[s:s + 1], ref, "bf16", vmax, f"seq {s} (n={n})")
+
+    def oracle_seq(snap):
+        s = snap["s"]
+        k2, v2 = oracle.reshape_and_cache_fp8_ref(case.new_key[s:s + 1], case.new_value[s:s + 1],
+                                                  snap["mk"], snap["mv"], snap["slot"],
+                                                  case.block_size, "bf16", K_SCALE, V_SCALE)
+        ref = oracle.decode_fp8_ref(case.query[s:s + 1], k2, v2, snap["table"],
+                                    np.array([snap["n"]], np.int32), case.block_size, case.scale,
+                                    "bf16", K_SCALE, V_SCALE)
+        V = oracle.resolve_sequence(oracle.dequantize_fp8(v2, V_SCALE), snap["table"][0],
+                                    snap["n"], case.block_size, "f64")
+        return ref[0], k2, v2, float(np.max(np.abs(V)))
+
+    compare_every_sequence(case, W.from_torch(out, "bf16"), kc, vc, snaps, oracle_seq,
+                           f"fp8 full size {name}", pool_dtype="fp8")
+    del kc, vc, case, snaps
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("heads", [(8, 8), (8, 2)])
