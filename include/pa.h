@@ -185,6 +185,29 @@ pa_status pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_se
                           void* stream);
 
 /*
+ * pa_decode_noalloc — pa_decode_ex for callers that cannot allocate device memory: code that a
+ * HIP graph captures, tight serving loops, hosts that forbid allocation.  The split-KV
+ * partials that pa_decode_ex keeps in the caller's workspace live instead in a fixed array of
+ * PA_DECODE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from the first
+ * call on that GPU until the process ends.  Arguments, results and errors are pa_decode_ex's
+ * without the workspace pair; a shape whose pa_decode_workspace_bytes exceeds the array
+ * returns PA_ERR_WORKSPACE before anything is launched (use pa_decode_ex with a workspace).
+ * The call allocates nothing and issues no memset.  Every call on one GPU uses that GPU's
+ * array: calls that can run at the same time on one GPU (on different streams, or from
+ * several threads) race on it and must be serialised by the caller; calls in order on one
+ * stream are safe.  The first call on a GPU looks up the array's device address
+ * (PA_ERR_LAUNCH if the runtime cannot).
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                            pa_dtype dtype, int32_t partition_size, pa_kernel kernel,
+                            uint32_t flags, void* stream);
+
+/*
  * pa_reshape_and_cache — store each new token's K and V at its physical slot.
  *
  * Every decode step appends the new token's key/value to its sequence's cache (jsqmd.com
