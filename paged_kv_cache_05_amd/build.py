@@ -32,6 +32,15 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source compiler options.  The 16-bit matrix-core decode keeps its MFMA accumulators in
+# ordinary VGPRs: left to its heuristics the compiler put them in AGPRs (about 250 registers,
+# two waves per SIMD) and copied all 32 of them into VGPRs on every chunk for the rarely taken
+# rescale; in VGPRs the kernel needs 164-174 registers and runs three waves per SIMD.
+EXTRA_FLAGS = {
+    "pa_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -45,7 +54,7 @@ def sources():
 
 def _compile(src: pathlib.Path, verbose: bool) -> pathlib.Path:
     obj = BUILD / (src.stem + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src.name, []), "-c", str(src), "-o", str(obj)]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

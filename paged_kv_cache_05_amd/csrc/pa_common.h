@@ -222,6 +222,7 @@ struct DecodeParams {
   int32_t max_blocks_per_seq, num_blocks;
   int32_t partition;         // tokens per partition (multiple of 16)
   int32_t max_parts;         // partitions a full table can hold
+  int32_t parts_per_wg;      // consecutive partitions one matrix-core workgroup walks (1, 2, 4)
   float scale_log2;          // scale * log2(e) (times the key scale of an 8-bit cache)
   float v_scale;             // value scale of an 8-bit cache (1 otherwise)
 };

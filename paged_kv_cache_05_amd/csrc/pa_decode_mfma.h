@@ -28,7 +28,14 @@
 // Softmax state: a running reference point per head, shared by the four lanes holding that head
 // (two permlane swaps per chunk for the chunk max); accumulators are rescaled only when
 // some head's max passes its reference point by more than 2^8.
-// Partitions, wave interleaving, prefetch and the final merge follow the vector-ALU kernel.
+// Partitions.  A workgroup walks parts_per_wg consecutive partitions of one (sequence, KV head)
+// (the host picks up to ~1024 tokens' worth when the grid stays large; one partition otherwise).
+// Wave w takes chunks w, w+4, ... of the whole run, so with partitions of a multiple of 128
+// tokens every wave holds the same number of chunks of each full partition.  When a wave has
+// consumed its last chunk of a partition it leaves its state in that partition's LDS slot once
+// the loads of its next chunk are issued (two chunks stay in flight); the last wave to finish
+// the workgroup merges every partition's partial, so no wave waits for another.  The query and
+// table prologue is paid once per workgroup.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -55,8 +62,9 @@ template <> struct Mfma<DT::BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
   }
-  __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
-  __device__ __forceinline__ static float value(uint32_t b) { return __uint_as_float(b << 16); }
+  // values of the low and high 16-bit halves of a packed word
+  __device__ __forceinline__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ __forceinline__ static float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
   __device__ __forceinline__ static uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
   }
@@ -70,9 +78,11 @@ template <> struct Mfma<DT::F16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
-  __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
-  __device__ __forceinline__ static float value(uint32_t b) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  __device__ __forceinline__ static float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+  }
+  __device__ __forceinline__ static float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
   }
   __device__ __forceinline__ static uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
@@ -109,8 +119,9 @@ struct Chunk8 { uint4 k[2]; uint2 v[4]; };
 
 // With an 8-bit cache the kernel is asked for three workgroups per CU: the compiler then fits it
 // in <= 168 registers (three waves per SIMD, no spills), and the extra wave hides the loads of
-// the shorter 8-bit chunks (GQA long, E4M3: 163-171 -> 133-140 us).  The 16-bit instances keep
-// the compiler's own choice (224-232 registers, two waves): three waves measured within +-2%.
+// the shorter 8-bit chunks.  The 16-bit instances are built with their MFMA accumulators in
+// ordinary VGPRs (176-180 registers, two waves per SIMD); asked for three waves they spill 7-10
+// values and ran GQA long-context batches 13% slower.
 template <DT dt, DT kt, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int D = 128;
@@ -129,20 +140,21 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
   const int lr = lane & 15, kg = lane >> 4;
 
-  // Workgroups are dealt round-robin to the 8 XCDs (id mod 8); the partition index is the
+  // Workgroups are dealt round-robin to the 8 XCDs (id mod 8); the partition-group index is the
   // slowest grid index so every XCD gets an even share of (sequence, head) units.
   const int units = p.num_seqs * p.num_kv_heads * p.head_chunks;
-  const int part = blockIdx.x / units;
-  const int unit = blockIdx.x - part * units;
+  const int pg = blockIdx.x / units;
+  const int unit = blockIdx.x - pg * units;
   const int hc = unit % (p.num_kv_heads * p.head_chunks);
   const int s = unit / (p.num_kv_heads * p.head_chunks);
   const int g = hc / p.head_chunks;
   const int h0 = g * p.group + (hc % p.head_chunks) * GT;
+  const int p0 = pg * p.parts_per_wg;   // first partition of this workgroup
   // Workgroups past a sequence's last partition leave before any vector load (as in the
   // vector-ALU kernel); partition 0 always has work.
-  if (part > 0) {
+  if (p0 > 0) {
     const int n0 = min(p.context_lens[s], p.max_blocks_per_seq * BS);
-    if (part * p.partition >= n0) return;
+    if (p0 * p.partition >= n0) return;
   }
 
   // Loads independent of the context length first (their latency overlaps the read of
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   // (entries past the sequence's end are loaded but never used; all lie inside the row).
   const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const int ch_begin = part * (p.partition / 16);
+  const int ch_begin = p0 * (p.partition / 16);
   uint4 qb[4];  // Q^T operand (unscaled 16-bit values): chunk kc holds Q[h][32kc + 8kg .. +8]
   {
     const char* qp = (const char*)p.q + (q_row0 + (size_t)(lr % GT) * D) * EB;
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   int n = p.context_lens[s];
   n = min(n, p.max_blocks_per_seq * BS);
   const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
-  if (part >= nparts) return;
+  if (p0 >= nparts) return;
   if (n <= 0) {  // empty context: the output is defined as zero
     if (threadIdx.x < GT * 16)
       *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
@@ -188,8 +200,10 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int t_end = min(n, (part + 1) * p.partition);
+  const int np_wg = min(nparts, p0 + p.parts_per_wg) - p0;   // partitions of this workgroup
+  const int t_end = min(n, (p0 + np_wg) * p.partition);
   const int ch_end = (t_end + 15) / 16;
+  const int Q = p.partition / 64;   // a wave's chunks in each full partition (used if np_wg > 1)
   const size_t head_off = (size_t)g * BS * D;
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
   const int v_off = (4 * kg * D + 8 * lr) * EBK;   // V rows: token 4kg (+j), dims 8lr..
@@ -225,6 +239,50 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       else c.v[j] = load_kv<STREAM>(vp + j * ROW);
     }
   };
+  // End of partition p0 + k for this wave: it leaves its state (running max, denominator,
+  // unnormalised outputs) in the partition's LDS slot and starts the next partition afresh.
+  // Slots are never reused within a workgroup (the host gives a workgroup at most NBUF
+  // partitions: 4, 2, 1 at 4, 8, 16 heads, 32 KiB of slots each), so no wave waits for another:
+  // the last wave to finish the workgroup merges every partition (see the end of the kernel).
+  constexpr int NBUF = GT == 4 ? 4 : GT == 8 ? 2 : 1;
+  __shared__ float s_o[NBUF][4][GT][D];
+  __shared__ float s_m[NBUF][4][GT], s_l[NBUF][4][GT];
+  __shared__ int s_done;
+  if (threadIdx.x == 0) s_done = 0;
+  __syncthreads();
+  auto flush = [&](int k) {
+    // this wave's denominator per head: sum the four token groups
+    float lt = l_run + __shfl_xor(l_run, 16);
+    lt += __shfl_xor(lt, 32);
+    if (kg * 4 < GT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_o[k][wave][kg * 4 + i][8 * lr + e] = acc[e][i];
+    }
+    if (lane < GT) {
+      s_m[k][wave][lane] = m_run;
+      s_l[k][wave][lane] = lt;
+    }
+    m_run = -INFINITY;
+    l_run = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // A consumed chunk that ends one of the workgroup's non-final partitions (those are full: Q
+  // chunks per wave, Q even) leaves that partition pending; settle() flushes it right after the
+  // next chunk's loads are issued.  Such a chunk has an odd index in the wave's run (Q even), so
+  // it is always the second of an unrolled pair below, and every 64-chunk table block starts on
+  // an even index: settling at the top of each pair, of each block and before a lone last chunk
+  // is enough.
+  int pending = -1;
+  auto settle = [&]() {
+    if (pending >= 0) {
+      flush(pending);
+      pending = -1;
+    }
+  };
+
   // okm: bit b set when the chunk's block b has a valid id (both bits for blocks >= 16); this
   // lane's tokens 4kg .. 4kg+3 lie in block kg/2 of an 8-token pair
   auto consume = [&](Chunk& c, int ch, int okm) {
@@ -287,16 +345,19 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       m_run = grow ? mn : m_run;
     }
     const float ms = safe_max(m_run);
-    uint32_t hi[4], lo[4];
+    float pv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float pj = fast_exp2(sv[j] - ms);
-      l_run += pj;
-      hi[j] = M::bits(pj);
-      lo[j] = M::bits(pj - M::value(hi[j]));
+      pv[j] = fast_exp2(sv[j] - ms);
+      l_run += pv[j];
     }
-    const uint2 phi = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    const uint2 plo = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    // 16-bit high parts of the probabilities (two per word, token 4kg + j in half j % 2), then
+    // the 16-bit remainders p - high: packed round-to-nearest-even conversions, one instruction
+    // per pair (the probabilities are finite and non-negative)
+    const uint32_t h01 = M::pack2(pv[0], pv[1]), h23 = M::pack2(pv[2], pv[3]);
+    const uint2 phi = make_uint2(h01, h23);
+    const uint2 plo = make_uint2(M::pack2(pv[0] - M::lo(h01), pv[1] - M::hi(h01)),
+                                 M::pack2(pv[2] - M::lo(h23), pv[3] - M::hi(h23)));
     uint4 vb[4];   // this lane's 4 V rows (dims 8lr .. +8) as 16-bit values
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -312,6 +373,10 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       const uint2 bv = tile_column(vb, e);
       acc[e] = M::mma16(phi, bv, acc[e]);
       acc[e] = M::mma16(plo, bv, acc[e]);
+    }
+    if (np_wg > 1) {
+      const int j = (ch - ch_begin) >> 2;   // this wave's chunk index in the workgroup's run
+      if ((j + 1) % Q == 0 && (j + 1) / Q < np_wg) pending = (j + 1) / Q - 1;
     }
   };
 
@@ -350,11 +415,13 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     phys_of(0, oka);
     load_chunk(ca, ph0, ph1, base);
     __builtin_amdgcn_sched_barrier(0);
+    settle();
     int i = 0;
     for (; i + 2 < cnt; i += 2) {
       phys_of(i + 1, okb);
       load_chunk(cb, ph0, ph1, base + 4 * (i + 1));
       __builtin_amdgcn_sched_barrier(0);
+      settle();
       consume(ca, base + 4 * i, oka);
       phys_of(i + 2, oka);
       load_chunk(ca, ph0, ph1, base + 4 * (i + 2));
@@ -365,44 +432,40 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       phys_of(i + 1, okb);
       load_chunk(cb, ph0, ph1, base + 4 * (i + 1));
       __builtin_amdgcn_sched_barrier(0);
+      settle();
       consume(ca, base + 4 * i, oka);
       consume(cb, base + 4 * (i + 1), okb);
     } else {
+      settle();   // the loop's last pair may have ended a partition; no load is left to overlap
       consume(ca, base + 4 * i, oka);
     }
   }
+  settle();
+  flush(np_wg - 1);   // the workgroup's final partition (possibly partial, possibly empty here)
 
-  // this wave's denominator per head: sum the four token groups
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
-
-  __shared__ float s_o[4][GT][D];
-  __shared__ float s_m[4][GT], s_l[4][GT];
-  if (kg * 4 < GT) {
+  // The last of the four waves to get here merges every partition of the workgroup into its
+  // partial (or into the output when the sequence has one partition).  Each wave's LDS writes
+  // complete before it counts itself in.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  int before = 0;
+  if (lane == 0) before = atomicAdd(&s_done, 1);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before != 3) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  for (int t = lane; t < np_wg * GT * 16; t += kWave) {
+    const int k = t / (GT * 16), h = (t / 16) % GT, cc = t % 16;
+    float Mx = s_m[k][0][h];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][kg * 4 + i][8 * lr + e] = acc[e][i];
-  }
-  if (lane < GT) {
-    s_m[wave][lane] = m_run;
-    s_l[wave][lane] = lt;
-  }
-  __syncthreads();
-  if (threadIdx.x < GT * 16) {
-    const int h = threadIdx.x / 16, cc = threadIdx.x % 16;
-    float Mx = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+    for (int w = 1; w < 4; ++w) Mx = fmaxf(Mx, s_m[k][w][h]);
     const float ms = safe_max(Mx);
     float L = 0.0f, O[8] = {};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // waves hold unnormalised sums relative to their own max: rescale both to M
-      const float wt = fast_exp2(s_m[w][h] - ms);
-      L = fmaf(wt, s_l[w][h], L);
+      const float wt = fast_exp2(s_m[k][w][h] - ms);
+      L = fmaf(wt, s_l[k][w][h], L);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) O[e] = fmaf(wt, s_o[w][h][cc * 8 + e], O[e]);
+      for (int e = 0; e < 8; ++e) O[e] = fmaf(wt, s_o[k][w][h][cc * 8 + e], O[e]);
     }
     const float inv = p.v_scale / L;   // an 8-bit cache's value scale factors out of the sum
 #pragma unroll
@@ -411,7 +474,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     if (nparts == 1) {
       *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * 8) * EB) = Elem<dt>::pack(O);
     } else {
-      const size_t slot = ((size_t)s * p.num_heads + h0 + h) * p.max_parts + part;
+      const size_t slot = ((size_t)s * p.num_heads + h0 + h) * p.max_parts + p0 + k;
       float* po = p.ws_o + slot * D + cc * 8;
       *reinterpret_cast<float4*>(po) = make_float4(O[0], O[1], O[2], O[3]);
       *reinterpret_cast<float4*>(po + 4) = make_float4(O[4], O[5], O[6], O[7]);
@@ -420,8 +483,13 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   }
 }
 
+
+
+
 template <DT dt, DT kt, int BS, bool ST>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
+  // the kernel holds LDS slots for at most 4, 2, 1 partitions at 4, 8, 16 heads per workgroup
+  if (p.parts_per_wg < 1 || p.parts_per_wg > (gt == 4 ? 4 : gt == 8 ? 2 : 1)) return hipErrorInvalidValue;
   switch (gt) {
     case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
     case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
