@@ -571,7 +571,6 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                              max_blocks_per_seq, partition_size);
   if (st != PA_OK) return st;
-  if (head_dim != 128) return PA_ERR_UNSUPPORTED;
   if ((flags & ~PA_DECODE_SHARED_BLOCKS) != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   if (num_blocks <= 0) return PA_ERR_BAD_SHAPE;

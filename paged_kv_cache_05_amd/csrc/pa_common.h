@@ -270,6 +270,9 @@ hipError_t launch_decode_valu_bf16(int head_dim, int block_size, int heads_per_w
                                    const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_decode_valu_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
                                   bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_valu_fp8_dims(DT dt, int head_dim, int block_size, int heads_per_wg,
+                                       bool stream_kv, const DecodeParams& p, int grid,
+                                       hipStream_t st);
 hipError_t launch_reshape_and_cache_fp8(DT dt, const void* key, const void* value, void* kc,
                                         void* vc, const int64_t* slots, int num_tokens,
                                         int head_dim, int block_size, int num_blocks,

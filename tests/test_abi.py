@@ -221,7 +221,10 @@ def test_fp8_argument_errors(lib):
     assert call({0: None}) == 1
     assert call({14: 0}) == 3               # f32 queries
     assert call({14: 3}) == 3               # an 8-bit query type
-    assert call({9: 64}) == 3               # head_dim 64
+    assert call({9: 96}) == 3               # head_dim 96
+    assert call({9: 64, 0: None}) == 1      # head dims 64, 80, 256 accepted (then null output)
+    assert call({9: 80, 0: None}) == 1
+    assert call({9: 256, 0: None}) == 1
     assert call({20: 2}) == 3               # unknown flag
     assert call({15: float("inf")}) == 2
     assert call({12: 64, 17: 64}) == 4      # split needs a workspace

@@ -20,9 +20,9 @@ K_SCALE = np.float32(W.FP8_DRAW_SCALE)       # pools drawn as N(0,1) / (1/64)
 V_SCALE = np.float32(W.FP8_DRAW_SCALE * 0.5)
 
 
-def _spec(dtype, bs, Hq, Hkv, lengths, seed, **kw):
+def _spec(dtype, bs, Hq, Hkv, lengths, seed, D=128, **kw):
     kw.setdefault("new_tokens", ("free", 0))
-    return W.CaseSpec("fp8", seed, len(lengths), Hq, Hkv, 128, dtype, bs, ("fixed", list(lengths)),
+    return W.CaseSpec("fp8", seed, len(lengths), Hq, Hkv, D, dtype, bs, ("fixed", list(lengths)),
                       kv_dtype="fp8", **kw)
 
 
@@ -82,6 +82,60 @@ def test_decode_fp8_matches_oracle(dtype, bs, Hq, Hkv, lengths, P):
     got = W.from_torch(out, dtype)
     vdeq = oracle.dequantize_fp8(case.value_cache, V_SCALE)
     assert_attention_close(got, _oracle(case), dtype, _vmax(case, vdeq), "decode_fp8")
+
+
+@pytest.mark.parametrize("D", [64, 80, 256])
+@pytest.mark.parametrize("dtype,bs,Hq,Hkv,P", [("bf16", 16, 8, 8, 0), ("f16", 8, 8, 2, 64),
+                                               ("bf16", 64, 4, 1, 128), ("bf16", 16, 16, 4, 256)])
+def test_decode_fp8_head_dims(D, dtype, bs, Hq, Hkv, P):
+    """8-bit caches at head dims 64, 80 (rows of 5 sixteen-byte vectors: 3 idle lanes per 8-lane
+    row) and 256, on the vector ALUs for every head grouping: against the oracle on the
+    dequantized pools, and bit-identical when every unread slot holds a NaN code and unused
+    table entries hold junk."""
+    import torch
+    dev = need_gpu()
+    lengths = (1, 15, 16, 17, 200, 1000, 2049)
+    spec = _spec(dtype, bs, Hq, Hkv, lengths, seed=240 + D + bs + Hq, D=D)
+    say(f"decode_fp8 D={D} {dtype} bs{bs} Hq{Hq} Hkv{Hkv} P={P}")
+    outs = []
+    for kw in ({}, {"poison": True, "table_fill": 2**31 - 1}):
+        case = W.build_case(spec, **kw)
+        q, kc, vc, bt, cl = _upload(case, dev)
+        out = torch.empty_like(q)
+        ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE),
+                       partition_size=P)
+        torch.cuda.synchronize()
+        outs.append(W.from_torch(out, dtype))
+        if not kw:
+            vdeq = oracle.dequantize_fp8(case.value_cache, V_SCALE)
+            assert_attention_close(outs[0], _oracle(case), dtype, _vmax(case, vdeq),
+                                   f"decode_fp8 D={D}")
+    assert np.array_equal(outs[1].view(np.uint16), outs[0].view(np.uint16))
+
+
+@pytest.mark.parametrize("D", [64, 80, 256])
+def test_fp8_step_head_dims(D):
+    """reshape_and_cache_fp8 then decode at head dims 64 / 80 / 256: the quantised writes are
+    bit-exact over the whole pool and the decode meets the bar against the oracle chain."""
+    import torch
+    dev = need_gpu()
+    spec = W.CaseSpec("fp8step", 250 + D, 5, 8, 2, D, "bf16", 16, ("fixed", [1, 16, 17, 300, 64]),
+                      kv_dtype="fp8")
+    case = W.build_case(spec)
+    q, kc, vc, bt, cl = _upload(case, dev)
+    nk, nv = W.to_torch(case.new_key, "bf16", dev), W.to_torch(case.new_value, "bf16", dev)
+    ops.reshape_and_cache_fp8(nk, nv, kc, vc, torch.from_numpy(case.slot_mapping).to(dev),
+                              float(K_SCALE), float(V_SCALE))
+    out = torch.empty_like(q)
+    ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE))
+    torch.cuda.synchronize()
+    k2, v2 = oracle.reshape_and_cache_fp8_ref(case.new_key, case.new_value, case.key_cache,
+                                              case.value_cache, case.slot_mapping, 16, "bf16",
+                                              K_SCALE, V_SCALE)
+    assert np.array_equal(W.from_torch(kc, "fp8"), k2)
+    assert np.array_equal(W.from_torch(vc, "fp8"), v2)
+    assert_attention_close(W.from_torch(out, "bf16"), _oracle(case, k2, v2), "bf16",
+                           _vmax(case, oracle.dequantize_fp8(v2, V_SCALE)), f"fp8 step D={D}")
 
 
 @pytest.mark.parametrize("heads", [(4, 4), (8, 2)])
