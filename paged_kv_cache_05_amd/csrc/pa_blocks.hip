@@ -10,10 +10,16 @@
 //
 // Concurrency.  Appends of different sequences run in parallel threads of one workgroup and
 // meet only in atomics: the free stack is popped with atomicSub on its top (the first `top`
-// decrements succeed, later ones undo theirs), and a sequence writing into its last block
-// takes one reference off it with atomicSub: if the count it saw was above 1 another holder
-// remains, so it copies into a fresh block; if it saw 1 it is the last holder and puts its
-// reference back.  Every outcome equals processing the sequences one at a time in some
+// decrements succeed, later ones undo theirs, so a failed pop means the stack is empty for the
+// rest of the call: nothing pushes during an append).  A sequence writing into a partly filled
+// last block takes one reference off it with atomicSub.  If the count it saw was above 1 another
+// holder remains, so it copies into a fresh block, or, with none left, puts its reference back
+// and fails.  If it saw 1 it may be the last holder, but a sharer whose copy failed may still
+// put its reference back: so it decides only after a barrier, once every copy of the batch has
+// succeeded or failed.  A count still at 0 means every other sharer moved to a copy and it
+// writes in place; otherwise a sharer stayed (the block is still shared) and, the stack being
+// empty, it fails as well, as it would in any one-at-a-time order.  Batches of 1024 sequences
+// run one after another.  Every outcome equals processing the sequences one at a time in some
 // order; which popped block a sequence gets, and which sharer keeps a shared block, depend on
 // that order.
 #include "pa_common.h"
@@ -39,7 +45,8 @@ __device__ __forceinline__ int pop_free(const EngineState& e, int32_t* status) {
   return b;
 }
 
-// One workgroup: thread i appends to sequence seq_ids[i] (then i + 1024, ...).
+// One workgroup: thread i appends to sequence seq_ids[i], then i + 1024, ... in batches
+// separated by barriers (every thread runs every batch, so the barriers pair up).
 __global__ __launch_bounds__(kAppendThreads) void append_slots_kernel(
     EngineState e, const int32_t* __restrict__ seq_ids, int n, int64_t* __restrict__ slots,
     int64_t* __restrict__ pairs, int32_t* __restrict__ num_pairs, int32_t* __restrict__ status) {
@@ -49,49 +56,67 @@ __global__ __launch_bounds__(kAppendThreads) void append_slots_kernel(
   }
   __syncthreads();
   const int bs = e.block_size;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int s = seq_ids[i];
+  for (int batch = 0; batch < n; batch += blockDim.x) {
+    const int i = batch + threadIdx.x;
     int64_t slot = -1;
-    if ((unsigned)s >= (unsigned)e.num_seqs) {       // not a sequence of these tables
-      atomicMax(status, 3);
-      slots[i] = slot;
-      continue;
-    }
-    const int len = e.context_lens[s];
-    const int j = len / bs, off = len - j * bs;
-    int32_t* row = e.tables + (size_t)s * e.max_blocks_per_seq;
-    if (len < 0 || j >= e.max_blocks_per_seq) {      // the table is full
-      atomicMax(status, 2);
-    } else if (off == 0) {                           // the last block is full: a fresh one
-      const int nb = pop_free(e, status);
-      if (nb >= 0) {
-        row[j] = nb;
-        e.ref_counts[nb] = 1;
-        slot = (int64_t)nb * bs;
-      }
-    } else if ((unsigned)row[j] >= (unsigned)e.num_blocks) {   // a broken table entry
-      atomicMax(status, 3);
-    } else {
-      const int b = row[j];
-      if (atomicSub(&e.ref_counts[b], 1) > 1) {      // another holder remains: copy on write
-        const int nb = pop_free(e, status);
-        if (nb < 0) {
-          atomicAdd(&e.ref_counts[b], 1);
+    int s = -1, len = 0, off = 0;
+    int last_block = -1;   // the partly filled last block this thread was last to let go of
+    if (i < n) {
+      s = seq_ids[i];
+      if ((unsigned)s >= (unsigned)e.num_seqs) {       // not a sequence of these tables
+        atomicMax(status, 3);
+        s = -1;
+      } else {
+        len = e.context_lens[s];
+        const int j = len / bs;
+        off = len - j * bs;
+        int32_t* row = e.tables + (size_t)s * e.max_blocks_per_seq;
+        if (len < 0 || j >= e.max_blocks_per_seq) {    // the table is full
+          atomicMax(status, 2);
+        } else if (off == 0) {                         // the last block is full: a fresh one
+          const int nb = pop_free(e, status);
+          if (nb >= 0) {
+            row[j] = nb;
+            e.ref_counts[nb] = 1;
+            slot = (int64_t)nb * bs;
+          }
+        } else if ((unsigned)row[j] >= (unsigned)e.num_blocks) {   // a broken table entry
+          atomicMax(status, 3);
         } else {
-          const int k = atomicAdd(num_pairs, 1);
-          pairs[2 * k] = b;
-          pairs[2 * k + 1] = nb;
-          e.ref_counts[nb] = 1;
-          row[j] = nb;
-          slot = (int64_t)nb * bs + off;
+          const int b = row[j];
+          if (atomicSub(&e.ref_counts[b], 1) > 1) {    // another holder remains: copy on write
+            const int nb = pop_free(e, status);
+            if (nb < 0) {
+              atomicAdd(&e.ref_counts[b], 1);          // no block left: keep the shared one
+            } else {
+              const int k = atomicAdd(num_pairs, 1);
+              pairs[2 * k] = b;
+              pairs[2 * k + 1] = nb;
+              e.ref_counts[nb] = 1;
+              row[j] = nb;
+              slot = (int64_t)nb * bs + off;
+            }
+          } else {
+            last_block = b;                            // decided after the barrier
+          }
         }
-      } else {                                       // the last holder: write in place
-        atomicAdd(&e.ref_counts[b], 1);
-        slot = (int64_t)b * bs + off;
       }
     }
-    if (slot >= 0) e.context_lens[s] = len + 1;
-    slots[i] = slot;
+    __syncthreads();   // every copy decision of this batch (and every put-back) is done
+    if (last_block >= 0) {
+      if (atomicAdd(&e.ref_counts[last_block], 0) == 0) {   // every other sharer moved off
+        atomicAdd(&e.ref_counts[last_block], 1);
+        slot = (int64_t)last_block * bs + off;
+      } else {                                         // still shared and no block left
+        atomicAdd(&e.ref_counts[last_block], 1);
+        atomicMax(status, 1);
+      }
+    }
+    if (i < n) {
+      if (slot >= 0) e.context_lens[s] = len + 1;
+      slots[i] = slot;
+    }
+    __syncthreads();   // the next batch sees this one's counts and lengths
   }
 }
 

@@ -244,3 +244,81 @@ def test_device_step_fork_append_copy_decode():
     ops.decode(out, gq, gk, gv, d[0][S:].contiguous(), d[1][S:].contiguous(), D ** -0.5)
     torch.cuda.synchronize()
     assert_attention_close(W.from_torch(out, "bf16"), sib, "bf16", vmax, "siblings")
+
+
+def _outcome(ctx_before, tables_before, slots, ctx_after, refs_after, status, seqs, bs, shared):
+    """What a parallel or sequential append decided, independent of which free block each
+    copy received: per appender 'fail', 'in place' or 'copy'; the lengths; the status; the
+    reference counts of the shared blocks."""
+    kinds = []
+    for i, s in enumerate(seqs):
+        n = int(ctx_before[s])
+        if slots[i] < 0:
+            kinds.append("fail")
+        elif int(slots[i]) // bs == int(tables_before[s, n // bs]):
+            kinds.append("in place")
+        else:
+            kinds.append("copy")
+    return (tuple(kinds), tuple(int(x) for x in ctx_after), int(status),
+            tuple(int(refs_after[b]) for b in shared))
+
+
+# (sharers of each shared partial block, free blocks): a block shared by k sequences that all
+# append is copied min(k - 1, free) times in any one-at-a-time order, and its last holder writes
+# in place only when every other sharer got a copy
+EXHAUSTED = [((2,), 0), ((2,), 1), ((4,), 1), ((4,), 2), ((3, 2), 1), ((3, 2), 2), ((2, 2, 2), 2)]
+
+
+@pytest.mark.parametrize("sharers,free", EXHAUSTED)
+def test_append_shared_blocks_with_too_few_free(sharers, free):
+    """Sequences sharing partly filled last blocks (as after parallel-sampling forks) all append
+    while the free stack holds fewer blocks than the copies would need.  Repeated 100 times from
+    the same state, every parallel outcome must be one that appending the sequences one at a
+    time, in some order, produces (all orders are enumerated with the oracle): a sequence may
+    write in place only once no other sequence still holds its block."""
+    import itertools
+    import torch
+    dev = need_gpu()
+    bs = 4
+    tables, ctx, shared = [], [], []
+    NB = len(sharers) + free                   # the shared blocks and the free ones
+    for b, k in enumerate(sharers):
+        shared.append(b)
+        for _ in range(k):
+            tables.append([b, -1])
+            ctx.append(2)                     # two tokens in the shared block
+    tables = np.array(tables, np.int32)
+    ctx = np.array(ctx, np.int32)
+    refs = np.zeros(NB, np.int32)
+    for b, k in enumerate(sharers):
+        refs[b] = k
+    stack = np.zeros(NB, np.int32)
+    stack[:free] = np.arange(len(sharers), NB, dtype=np.int32)
+    top = free
+    S = len(ctx)
+    seqs = np.arange(S, dtype=np.int32)
+    allowed = set()
+    for order in itertools.permutations(range(S)):
+        w = oracle.append_slots_ref(tables, ctx, refs, stack, top, np.array(order, np.int32), bs)
+        wslots = np.full(S, -1, np.int64)
+        for pos, s in enumerate(order):
+            wslots[s] = w[5][pos]
+        allowed.add(_outcome(ctx, tables, wslots, w[1], w[2], w[7], seqs, bs, shared))
+    say(f"shared {sharers}, free {free}: {len(allowed)} sequential outcomes")
+    seen = set()
+    for rep in range(100):
+        d = _dev_state((tables, ctx, refs, stack, top), dev)
+        slots = torch.full((S,), -7, dtype=torch.int64, device=dev)
+        pairs = torch.full((S, 2), -7, dtype=torch.int64, device=dev)
+        npairs = torch.zeros(1, dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        ops.append_slots(*d, torch.from_numpy(seqs).to(dev), bs, slots, pairs, npairs, status)
+        torch.cuda.synchronize()
+        gt, gc, gr, gs, gtop = _host(d)
+        got = _outcome(ctx, tables, slots.cpu().numpy(), gc, gr, int(status.item()), seqs, bs, shared)
+        assert got in allowed, (rep, got, allowed)
+        seen.add(got)
+        k = int(npairs.item())
+        assert k == sum(1 for x in got[0] if x == "copy")
+        assert int(gtop[0]) == top - k
+    say(f"  parallel outcomes seen: {len(seen)}")
