@@ -35,9 +35,11 @@ COMMON_FLAGS = [
 # Per-source compiler options.  The 16-bit matrix-core decode keeps its MFMA accumulators in
 # ordinary VGPRs: left to its heuristics the compiler put them in AGPRs (about 250 registers,
 # two waves per SIMD) and copied all 32 of them into VGPRs on every chunk for the rarely taken
-# rescale; in VGPRs the kernel needs 164-174 registers and runs three waves per SIMD.
+# rescale.  The 256-dim instances keep the compiler's choice: their 16 KiB chunks and 64
+# accumulators need more than the 256 VGPRs one wave can address.
 EXTRA_FLAGS = {
     "pa_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "pa_decode_mfma_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

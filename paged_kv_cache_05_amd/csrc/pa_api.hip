@@ -95,20 +95,22 @@ Plan make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_
 }
 
 bool mfma_eligible(DT dt, int D, int G, int partition) {
-  return (dt == DT::F16 || dt == DT::BF16) && D == 128 && G % 4 == 0 && partition % 16 == 0;
+  return (dt == DT::F16 || dt == DT::BF16) && (D == 64 || D == 128 || D == 256) && G % 4 == 0 &&
+         partition % 16 == 0;
 }
 
 // Consecutive partitions one matrix-core workgroup walks.  Walking several pays the query and
 // table prologue once per workgroup instead of once per partition, and each partition still
 // gets its own partial.  It needs partitions of a multiple of 128 tokens (the same number of
-// chunks per wave in each), at most 4 / 2 / 1 of them at 4 / 8 / 16 heads per workgroup (LDS
-// slots), and is used only while the grid keeps at least kTargetWorkgroups workgroups.  Up to
+// chunks per wave in each), at most as many as the kernel's 32 KiB of LDS slots hold (4, 2, 1
+// for heads x head dim up to 512, 1024, 2048), and is used only while the grid keeps at least
+// kTargetWorkgroups workgroups.  Up to
 // kGroupTokens tokens per workgroup: measured on GQA long-context batches, single partitions of
 // 1024 tokens stream faster (5.80 TB/s) than of 512 (5.60) or 2048 (5.72).
 constexpr long kGroupTokens = 1024;
-int mfma_parts_per_wg(int partition, int max_parts, long units, int heads_per_wg) {
+int mfma_parts_per_wg(int partition, int max_parts, long units, int heads_per_wg, int head_dim) {
   if (max_parts <= 1 || partition % 128 != 0) return 1;
-  const int cap = heads_per_wg == 4 ? 4 : heads_per_wg == 8 ? 2 : 1;
+  const int cap = std::min(4, 2048 / (heads_per_wg * head_dim));
   int ppw = 1;
   while (2 * ppw <= cap && 2L * ppw * partition <= kGroupTokens &&
          units * ((max_parts + 2 * ppw - 1) / (2 * ppw)) >= kTargetWorkgroups)
@@ -119,7 +121,7 @@ int mfma_parts_per_wg(int partition, int max_parts, long units, int heads_per_wg
 // Query heads one workgroup serves.  The vector-ALU kernel keeps head_dim/64 .. head_dim/8
 // fp32 outputs per lane per head, so wide heads get fewer per workgroup.
 int heads_per_wg(bool mfma, int G, int D) {
-  if (mfma) return G % 16 == 0 ? 16 : G % 8 == 0 ? 8 : 4;
+  if (mfma) return G % 16 == 0 && D <= 128 ? 16 : G % 8 == 0 ? 8 : 4;
   const int cap = D >= 256 ? 2 : D == 80 ? 4 : 8;
   for (int gt = cap; gt > 1; gt /= 2)
     if (G % gt == 0) return gt;
@@ -293,7 +295,7 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   p.v_scale = 1.0f;
 
   const long units = (long)num_seqs * num_kv_heads * p.head_chunks;
-  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt) : 1;
+  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt, head_dim) : 1;
   const long grid = mfma ? units * ((pl.max_parts + p.parts_per_wg - 1) / p.parts_per_wg)
                         : valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
@@ -585,7 +587,8 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   // Grouped heads (a multiple of 4) run on the matrix cores, which read each K/V byte once per
   // KV head; otherwise the vector-ALU kernel, at most 2 heads per workgroup (16 fp32 outputs
   // per lane per head).
-  const bool mfma = mfma_eligible(dt, head_dim, G, pl.partition);
+  // (the 8-bit matrix-core kernel is built for head dim 128)
+  const bool mfma = mfma_eligible(dt, head_dim, G, pl.partition) && head_dim == 128;
   const int gt = mfma ? heads_per_wg(true, G, head_dim) : std::min(heads_per_wg(false, G, head_dim), 2);
 
   pa::DecodeParams p;
@@ -609,7 +612,7 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   p.scale_log2 = scale * k_scale * 1.4426950408889634f;
   p.v_scale = v_scale;
   const long units = (long)num_seqs * num_kv_heads * p.head_chunks;
-  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt) : 1;
+  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt, head_dim) : 1;
   const long grid = mfma ? units * ((pl.max_parts + p.parts_per_wg - 1) / p.parts_per_wg)
                         : valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;

@@ -280,6 +280,10 @@ hipError_t launch_reshape_and_cache_fp8(DT dt, const void* key, const void* valu
                                         hipStream_t st);
 hipError_t launch_decode_mfma(DT dt, int head_dim, int block_size, int heads_per_wg,
                               bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_mfma_d64(DT dt, int block_size, int heads_per_wg, bool stream_kv,
+                                  const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_mfma_d256(DT dt, int block_size, int heads_per_wg, bool stream_kv,
+                                   const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_decode_mfma_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
                                   bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const PrefillParams& p,

@@ -1,7 +1,8 @@
 #pragma once
 // Paged decode attention for grouped-query attention on the matrix cores (gfx950): the kernel
-// template.  pa_decode_mfma.hip instantiates it for 16-bit caches, pa_decode_mfma_fp8.hip for
-// 8-bit E4M3 caches (in parallel translation units).
+// template, for head dims D = 64, 128 and 256.  pa_decode_mfma.hip (D = 128),
+// pa_decode_mfma_d64.hip and pa_decode_mfma_d256.hip instantiate it for 16-bit caches,
+// pa_decode_mfma_fp8.hip for 8-bit E4M3 caches at D = 128 (in parallel translation units).
 //
 // When G query heads share one KV head (the pages note that GQA/MQA shrinks the per-token KV
 // cache: UltraLAB summary of Kwon et al. (xasun.com), boundary note after §八), the G queries
@@ -11,18 +12,18 @@
 //
 // Tiling.  A wave consumes one 16-token chunk per step: a block of 16, a slice of a larger
 // block, or two blocks of 8 (then K loads 0-1 and lanes 0-31 of the V loads read the first).
-//   Scores: S^T[16 tokens x 16 cols] = K_chunk[16 x 128] * Q^T[128 x 16], four
+//   Scores: S^T[16 tokens x 16 cols] = K_chunk[16 x D] * Q^T[D x 16], D/32 (2, 4, 8)
 //     v_mfma_f32_16x16x32 ops.  Column n holds query head n mod GT (heads are replicated when
 //     GT < 16).  A operand (K): lane l holds K[token l%16][32kc + 8(l/16) .. +8]; B operand
 //     (Q^T): lane l holds Q[head (l%16) mod GT][same 8 dims].  Result: lane l, register i holds
 //     the score of token 4(l/16)+i for head (l%16) mod GT.
-//   Output: O[16 rows x 16 cols] += P[16 x 16 tokens] * V[16 tokens x 16 cols], eight
-//     v_mfma_f32_16x16x16 ops per column group e = 0..7, column n meaning dim 8n + e.  The A
-//     operand (P) of lane l is head (l%16) mod GT at tokens 4(l/16) .. +4: exactly the four
-//     scores the lane already holds, so P never moves between lanes.  The B operand needs four
-//     tokens of one column per lane: lane l loads dims 8(l%16) .. +8 of tokens 4(l/16) .. +4
-//     (each load instruction reads four whole 256-byte rows) and transposes the 4x8 16-bit
-//     tile in registers with v_perm_b32.
+//   Output: O[16 rows x 16 cols] += P[16 x 16 tokens] * V[16 tokens x 16 cols], two
+//     v_mfma_f32_16x16x16 ops per column group e = 0 .. D/16-1, column n meaning dim
+//     (D/16) n + e.  The A operand (P) of lane l is head (l%16) mod GT at tokens 4(l/16) .. +4:
+//     exactly the four scores the lane already holds, so P never moves between lanes.  The B
+//     operand needs four tokens of one column per lane: lane l loads dims (D/16)(l%16) .. of
+//     tokens 4(l/16) .. +4 (the 16 lanes of a token group cover whole rows) and transposes the
+//     4 x D/16 16-bit tile in registers with v_perm_b32.
 //   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group), so
 //   the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
 // Softmax state: a running reference point per head, shared by the four lanes holding that head
@@ -112,29 +113,79 @@ __device__ __forceinline__ uint2 load_kv8(const void* ptr) {
   }
 }
 
-// Raw chunk buffers: 16-bit cache (K: 4 loads of 4 token rows; V: this lane's 4 rows of 8
-// dims) or 8-bit cache (K: 2 loads of 8 token rows; V: 4 rows of 8 dims, 8 bytes each).
-struct Chunk16 { uint4 k[4]; uint4 v[4]; };
-struct Chunk8 { uint4 k[2]; uint2 v[4]; };
+// 4-byte K/V load (V pieces of an 8-bit cache at D = 64), streaming or cache-allocating
+template <bool STREAM>
+__device__ __forceinline__ uint32_t load_kv4(const void* ptr) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ptr));
+  else return *reinterpret_cast<const uint32_t*>(ptr);
+}
+
+// W consecutive 32-bit words (W = 1, 2 or a multiple of 4) in the fewest loads
+template <int W, bool STREAM>
+__device__ __forceinline__ void load_words(uint32_t (&w)[W], const char* ptr) {
+  if constexpr (W == 1) {
+    w[0] = load_kv4<STREAM>(ptr);
+  } else if constexpr (W == 2) {
+    const uint2 v = load_kv8<STREAM>(ptr);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+    static_assert(W % 4 == 0, "whole 16-byte vectors");
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = load_kv<STREAM>(ptr + 16 * i);
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// Column e of a 4 x 2W tile of 16-bit values held as 4 rows of W words (row j = token j, word q
+// = dims 2q, 2q+1): the 4 tokens' values of dim e, two per word, token order preserved.
+template <int W>
+__device__ __forceinline__ uint2 tile_column_words(const uint32_t (&r)[4][W], int e) {
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  const int q = e >> 1;
+  return make_uint2(__builtin_amdgcn_perm(r[1][q], r[0][q], sel),
+                    __builtin_amdgcn_perm(r[3][q], r[2][q], sel));
+}
+
+// Raw chunk buffers: K as NK 16-byte loads of whole token rows, V as this lane's 4 token rows
+// of D/16 dims, VW 32-bit words each (16-bit or 8-bit cache elements).
+template <int NK, int VW> struct ChunkBuf { uint4 k[NK]; uint32_t v[4][VW]; };
+
+// LDS slots for the per-partition wave states: at most 32 KiB, so 4, 2 or 1 partitions per
+// workgroup (heads per workgroup x head dim up to 512, 1024, 2048).
+constexpr int mfma_slots(int gt, int d) { return 2048 / (gt * d) >= 4 ? 4 : 2048 / (gt * d); }
 
 // With an 8-bit cache the kernel is asked for three workgroups per CU: the compiler then fits it
 // in <= 168 registers (three waves per SIMD, no spills), and the extra wave hides the loads of
 // the shorter 8-bit chunks.  The 16-bit instances are built with their MFMA accumulators in
 // ordinary VGPRs (176-180 registers, two waves per SIMD); asked for three waves they spill 7-10
 // values and ran GQA long-context batches 13% slower.
-template <DT dt, DT kt, int BS, int GT, bool STREAM>
+template <DT dt, DT kt, int D, int BS, int GT, bool STREAM>
 __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel(const DecodeParams p) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
   constexpr int EB = 2;            // query / output element bytes
   constexpr bool K8 = kt == DT::FP8;
   constexpr int EBK = K8 ? 1 : 2;  // cache element bytes
-  constexpr int ROW = D * EBK;     // token row: 256 bytes (16-bit cache) or 128 (8-bit)
-  using Chunk = std::conditional_t<K8, Chunk8, Chunk16>;
+  constexpr int ROW = D * EBK;     // token row in bytes
+  constexpr int KC = D / 32;       // 32-dim depth steps of the score product
+  constexpr int KCOL = D / 8;      // 16-byte columns (8 dims of 16-bit values) of a K row
+  constexpr int DPL = D / 16;      // output dims per lane: column groups of O
+  constexpr int NK = 16 * ROW / 1024;   // 1-KiB K loads per 16-token chunk
+  constexpr int TPL = 1024 / ROW;  // token rows per K load
+  constexpr int LPR = ROW / 16;    // lanes per token row in a K load
+  constexpr int VW = DPL * EBK / 4;     // 32-bit words of this lane's piece of a V row
+  using Chunk = ChunkBuf<NK, VW>;
   constexpr int CPB = BS >= 16 ? BS / 16 : 1;   // 16-token chunks per block
   constexpr int BPC = BS >= 16 ? 1 : 16 / BS;   // blocks per chunk (2 for 8-token blocks)
   static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
   using M = Mfma<dt>;
   static_assert(GT == 4 || GT == 8 || GT == 16, "heads per workgroup");
+  static_assert(GT * D <= 2048, "the partition slots must fit 32 KiB of LDS");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform
@@ -163,11 +214,11 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int ch_begin = p0 * (p.partition / 16);
-  uint4 qb[4];  // Q^T operand (unscaled 16-bit values): chunk kc holds Q[h][32kc + 8kg .. +8]
+  uint4 qb[KC];  // Q^T operand (unscaled 16-bit values): chunk kc holds Q[h][32kc + 8kg .. +8]
   {
     const char* qp = (const char*)p.q + (q_row0 + (size_t)(lr % GT) * D) * EB;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
+    for (int kc = 0; kc < KC; ++kc)
       qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
   }
   // table entries of chunk ch: its block, or its two 8-token blocks (the second lies past the
@@ -188,7 +239,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
   if (p0 >= nparts) return;
   if (n <= 0) {  // empty context: the output is defined as zero
-    if (threadIdx.x < GT * 16)
+    if (threadIdx.x < GT * D / 8)
       *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
           make_uint4(0, 0, 0, 0);
     return;
@@ -196,9 +247,9 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
 
   float m_run = -INFINITY;  // running max (log2 units) of head lr % GT
   float l_run = 0.0f;       // this lane's share of that head's denominator
-  f32x4 acc[8];
+  f32x4 acc[DPL];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int np_wg = min(nparts, p0 + p.parts_per_wg) - p0;   // partitions of this workgroup
   const int t_end = min(n, (p0 + np_wg) * p.partition);
@@ -206,22 +257,22 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   const int Q = p.partition / 64;   // a wave's chunks in each full partition (used if np_wg > 1)
   const size_t head_off = (size_t)g * BS * D;
   const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
-  const int v_off = (4 * kg * D + 8 * lr) * EBK;   // V rows: token 4kg (+j), dims 8lr..
+  const int v_off = (4 * kg * D + DPL * lr) * EBK;   // V rows: token 4kg (+j), dims DPL lr ..
 
-  // K arrives coalesced (load i, lane l: token 4i + l/16, 16-byte column l%16 -- each load
-  // instruction reads four whole rows) and is re-laid out through a wave-private 4 KiB LDS tile
-  // into the MFMA operand layout (token l%16, columns 4kc + l/16).  Loading the operand layout
-  // straight from HBM would cut every row into 64-byte pieces per instruction, which measured
-  // ~15% slower.  Slot of (token t, column c) is 16t + (c xor t): writes and operand reads both
+  // K arrives coalesced (load i, lane l: token TPL i + l / LPR, 16-byte piece l % LPR -- each
+  // load instruction reads whole rows) and is re-laid out through a wave-private LDS tile of 16
+  // tokens x KCOL columns into the MFMA operand layout (token l%16, columns 4kc + l/16).
+  // Loading the operand layout straight from HBM would cut every row into 64-byte pieces per
+  // instruction, which measured ~15% slower at D = 128.  Slot of (token t, column c) is
+  // KCOL t + (c xor swz(t)), swz(t) = t (t / 2 with 8 columns): writes and operand reads both
   // touch 16 distinct 16-byte bank groups per 16 lanes.
-  __shared__ uint4 s_k[4][256];
+  __shared__ uint4 s_k[4][16 * KCOL];
   uint4* kst = s_k[wave];
+  auto kslot = [](int t, int c) { return KCOL * t + (c ^ (KCOL >= 16 ? t : t >> 1)); };
 
   auto load_chunk = [&](Chunk& c, int phys0, int phys1, int ch) {
     const size_t el0 = (size_t)phys0 * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
-    // K: load i reads 1 KiB = 1024 / ROW token rows (4 or 8), lane l 16 bytes of it
-    constexpr int NK = K8 ? 2 : 4;
-    constexpr int TPL = 1024 / ROW;   // token rows per K load
+    // K: load i reads 1 KiB = TPL token rows, lane l 16 bytes of it
     const char* kp0 = (const char*)p.kc + el0 * EBK + lane * 16;
     const char* kp1 = kp0;
     const char* vp = (const char*)p.vc + el0 * EBK + v_off;
@@ -232,19 +283,17 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       if (kg >= 2) vp = (const char*)p.vc + el1 * EBK + v_off - 8 * ROW;
     }
 #pragma unroll
-    for (int i = 0; i < NK; ++i) c.k[i] = load_kv<STREAM>((i * TPL < 8 ? kp0 : kp1) + 1024 * i);
+    for (int i = 0; i < NK; ++i)   // token TPL i + lane / LPR: tokens 8-15 of an 8-token pair in phys1
+      c.k[i] = load_kv<STREAM>((TPL * i + lane / LPR < 8 ? kp0 : kp1) + 1024 * i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (K8) c.v[j] = load_kv8<STREAM>(vp + j * ROW);
-      else c.v[j] = load_kv<STREAM>(vp + j * ROW);
-    }
+    for (int j = 0; j < 4; ++j) load_words<VW, STREAM>(c.v[j], vp + j * ROW);
   };
   // End of partition p0 + k for this wave: it leaves its state (running max, denominator,
   // unnormalised outputs) in the partition's LDS slot and starts the next partition afresh.
   // Slots are never reused within a workgroup (the host gives a workgroup at most NBUF
   // partitions: 4, 2, 1 at 4, 8, 16 heads, 32 KiB of slots each), so no wave waits for another:
   // the last wave to finish the workgroup merges every partition (see the end of the kernel).
-  constexpr int NBUF = GT == 4 ? 4 : GT == 8 ? 2 : 1;
+  constexpr int NBUF = mfma_slots(GT, D);
   __shared__ float s_o[NBUF][4][GT][D];
   __shared__ float s_m[NBUF][4][GT], s_l[NBUF][4][GT];
   __shared__ int s_done;
@@ -258,7 +307,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_o[k][wave][kg * 4 + i][8 * lr + e] = acc[e][i];
+        for (int e = 0; e < DPL; ++e) s_o[k][wave][kg * 4 + i][DPL * lr + e] = acc[e][i];
     }
     if (lane < GT) {
       s_m[k][wave][lane] = m_run;
@@ -267,7 +316,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     m_run = -INFINITY;
     l_run = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < DPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
   // A consumed chunk that ends one of the workgroup's non-final partitions (those are full: Q
   // chunks per wave, Q even) leaves that partition pending; settle() flushes it right after the
@@ -288,26 +337,26 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   auto consume = [&](Chunk& c, int ch, int okm) {
     const bool ok = ((okm >> (BPC == 1 ? 0 : kg >> 1)) & 1) != 0;
     if constexpr (K8) {
-      // lane l of load i holds 16 codes: token 8i + l/8, dims 16(l%8) .. +15, which become the
-      // 16-bit columns 2(l%8) and 2(l%8)+1 of that token
+      // lane l of load i holds 16 codes: token TPL i + l / LPR, dims 16 (l % LPR) .. +15, which
+      // become the 16-bit columns 2 (l % LPR) and 2 (l % LPR) + 1 of that token
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = 8 * i + (lane >> 3), c0 = 2 * (lane & 7);
+      for (int i = 0; i < NK; ++i) {
+        const int t = TPL * i + lane / LPR, c0 = 2 * (lane % LPR);
         const uint2 a = fp8x4_to_16bit<M>(c.k[i].x), b = fp8x4_to_16bit<M>(c.k[i].y);
         const uint2 d = fp8x4_to_16bit<M>(c.k[i].z), e = fp8x4_to_16bit<M>(c.k[i].w);
-        kst[16 * t + (c0 ^ t)] = make_uint4(a.x, a.y, b.x, b.y);
-        kst[16 * t + ((c0 + 1) ^ t)] = make_uint4(d.x, d.y, e.x, e.y);
+        kst[kslot(t, c0)] = make_uint4(a.x, a.y, b.x, b.y);
+        kst[kslot(t, c0 + 1)] = make_uint4(d.x, d.y, e.x, e.y);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kst[16 * (4 * i + kg) + (lr ^ (4 * i + kg))] = c.k[i];
+      for (int i = 0; i < NK; ++i) kst[kslot(TPL * i + lane / LPR, lane % LPR)] = c.k[i];
     }
-    uint4 kop[4];
+    uint4 kop[KC];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) kop[kc] = kst[16 * lr + ((4 * kc + kg) ^ lr)];
+    for (int kc = 0; kc < KC; ++kc) kop[kc] = kst[kslot(lr, 4 * kc + kg)];
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) st = M::mma32(kop[kc], qb[kc], st);
+    for (int kc = 0; kc < KC; ++kc) st = M::mma32(kop[kc], qb[kc], st);
     const int tok0 = ch * 16 + 4 * kg;   // token of register j is tok0 + j
     const bool full = okm == 3 && (ch * 16 + 16 <= t_end);
     float sv[4];
@@ -319,8 +368,8 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
         const bool valid = ok && (tok0 + j < t_end);
         sv[j] = valid ? sv[j] : -INFINITY;
         if (!valid) {   // masked rows may hold NaN
-          if constexpr (K8) c.v[j] = make_uint2(0, 0);
-          else c.v[j] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int w = 0; w < VW; ++w) c.v[j][w] = 0;
         }
       }
     }
@@ -329,7 +378,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     const float bm = row_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     // Lazy reference point: it moves only when a head's max exceeds it by more than kLazy
     // (always on the first live chunk, from -inf), so probabilities stay below 2^kLazy and the
-    // rescale -- four cross-lane shuffles and 32 multiplies -- runs on few chunks instead of on
+    // rescale -- four cross-lane shuffles and 4 D/16 multiplies -- runs on few chunks instead of on
     // every chunk that sets a new max.  Any reference point gives the same o / l.
     const float mn = fmaxf(m_run, bm);
     const bool grow = mn > m_run + kLazy;
@@ -340,7 +389,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       for (int i = 0; i < 4; ++i) {
         const float a = __shfl(alpha, (kg * 4 + i) % GT);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e][i] *= a;
+        for (int e = 0; e < DPL; ++e) acc[e][i] *= a;
       }
       m_run = grow ? mn : m_run;
     }
@@ -358,19 +407,24 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     const uint2 phi = make_uint2(h01, h23);
     const uint2 plo = make_uint2(M::pack2(pv[0] - M::lo(h01), pv[1] - M::hi(h01)),
                                  M::pack2(pv[2] - M::lo(h23), pv[3] - M::hi(h23)));
-    uint4 vb[4];   // this lane's 4 V rows (dims 8lr .. +8) as 16-bit values
+    uint32_t vb[4][DPL / 2];   // this lane's 4 V rows (dims DPL lr ..) as 16-bit values
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (K8) {
-        const uint2 a = fp8x4_to_16bit<M>(c.v[j].x), b = fp8x4_to_16bit<M>(c.v[j].y);
-        vb[j] = make_uint4(a.x, a.y, b.x, b.y);
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+          const uint2 a = fp8x4_to_16bit<M>(c.v[j][w]);
+          vb[j][2 * w] = a.x;
+          vb[j][2 * w + 1] = a.y;
+        }
       } else {
-        vb[j] = c.v[j];
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vb[j][w] = c.v[j][w];
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint2 bv = tile_column(vb, e);
+    for (int e = 0; e < DPL; ++e) {
+      const uint2 bv = tile_column_words<DPL / 2>(vb, e);
       acc[e] = M::mma16(phi, bv, acc[e]);
       acc[e] = M::mma16(plo, bv, acc[e]);
     }
@@ -452,8 +506,9 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   before = __builtin_amdgcn_readfirstlane(before);
   if (before != 3) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  for (int t = lane; t < np_wg * GT * 16; t += kWave) {
-    const int k = t / (GT * 16), h = (t / 16) % GT, cc = t % 16;
+  constexpr int CPH = D / 8;   // 8-dim pieces of a head's output
+  for (int t = lane; t < np_wg * GT * CPH; t += kWave) {
+    const int k = t / (GT * CPH), h = (t / CPH) % GT, cc = t % CPH;
     float Mx = s_m[k][0][h];
 #pragma unroll
     for (int w = 1; w < 4; ++w) Mx = fmaxf(Mx, s_m[k][w][h]);
@@ -486,24 +541,30 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
 
 
 
-template <DT dt, DT kt, int BS, bool ST>
+template <DT dt, DT kt, int D, int BS, bool ST>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
-  // the kernel holds LDS slots for at most 4, 2, 1 partitions at 4, 8, 16 heads per workgroup
-  if (p.parts_per_wg < 1 || p.parts_per_wg > (gt == 4 ? 4 : gt == 8 ? 2 : 1)) return hipErrorInvalidValue;
+  // the kernel holds LDS slots for mfma_slots(gt, D) partitions (and 16 heads need D <= 128)
+  if (gt * D > 2048 || p.parts_per_wg < 1 || p.parts_per_wg > mfma_slots(gt, D))
+    return hipErrorInvalidValue;
   switch (gt) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, BS, 16, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 16:
+      if constexpr (D <= 128) {
+        hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 16, ST>), dim3(grid), dim3(256), 0, st, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <DT dt, DT kt>
+template <DT dt, DT kt, int D>
 hipError_t launch_bs(int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
   auto go = [&](auto bs_tag) -> hipError_t {
     constexpr int BS = decltype(bs_tag)::value;
-    return sk ? launch_gt<dt, kt, BS, true>(gt, p, grid, st) : launch_gt<dt, kt, BS, false>(gt, p, grid, st);
+    return sk ? launch_gt<dt, kt, D, BS, true>(gt, p, grid, st) : launch_gt<dt, kt, D, BS, false>(gt, p, grid, st);
   };
   switch (bs) {
     case 8: return go(std::integral_constant<int, 8>{});

@@ -9,8 +9,8 @@ hipError_t launch_decode_mfma_fp8(DT dt, int head_dim, int block_size, int heads
                                   bool stream_kv, const DecodeParams& p, int grid, hipStream_t st) {
   if (head_dim != 128) return hipErrorInvalidValue;
   switch (dt) {
-    case DT::F16: return launch_bs<DT::F16, DT::FP8>(block_size, heads_per_wg, stream_kv, p, grid, st);
-    case DT::BF16: return launch_bs<DT::BF16, DT::FP8>(block_size, heads_per_wg, stream_kv, p, grid, st);
+    case DT::F16: return launch_bs<DT::F16, DT::FP8, 128>(block_size, heads_per_wg, stream_kv, p, grid, st);
+    case DT::BF16: return launch_bs<DT::BF16, DT::FP8, 128>(block_size, heads_per_wg, stream_kv, p, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,7 +27,7 @@ def _case(dtype, D, BS, Hq, Hkv, lengths=EDGE_LENGTHS, seed=100, **kw):
 
 
 def _mfma_ok(dtype, D, Hq, Hkv, P):
-    return dtype in ("f16", "bf16") and D == 128 and (Hq // Hkv) % 4 == 0 and P % 16 == 0
+    return dtype in ("f16", "bf16") and D in (64, 128, 256) and (Hq // Hkv) % 4 == 0 and P % 16 == 0
 
 
 def _decode_matrix():
@@ -112,6 +112,31 @@ def test_head_dims_80_256(dtype, D, BS, heads):
     for P in (0, 128):
         assert_attention_close(u.decode("valu", P), oracle_decode(c), dtype, live_vmax(c),
                                f"D{D}/BS{BS}/G{Hq // Hkv}/P{P}")
+
+
+@pytest.mark.parametrize("heads", [(8, 2), (16, 2), (32, 2)])
+@pytest.mark.parametrize("BS", [8, 16, 64])
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mfma_head_dims_64_256(dtype, D, BS, heads):
+    """The matrix-core kernel at head dims 64 (8 LDS columns per K row, 4 output dims per lane)
+    and 256 (32 columns, 16 dims per lane, at most 8 heads per workgroup) with 4, 8 and 16 query
+    heads per KV head, single pass and split, against the oracle; NaN in every unread slot and
+    junk in unused table entries change no bit."""
+    dev = need_gpu()
+    Hq, Hkv = heads
+    lengths = [1, 15, 16, 17, 65, 300, 1000]
+    say(f"mfma {dtype} D={D} BS={BS} Hq={Hq} Hkv={Hkv}")
+    spec = W.CaseSpec(f"mfma_{dtype}_{D}_{BS}_{Hq}", D + BS + Hq + 3, len(lengths), Hq, Hkv, D,
+                      dtype, BS, ("fixed", lengths), new_tokens=("free", 0))
+    c = W.build_case(spec)
+    bad = W.build_case(spec, poison=True, table_fill=2**31 - 1)
+    u, ub = Uploaded(c, dev), Uploaded(bad, dev)
+    for P in (0, 64, 128):
+        got = u.decode("mfma", P)
+        assert_attention_close(got, oracle_decode(c), dtype, live_vmax(c),
+                               f"mfma D{D}/BS{BS}/G{Hq // Hkv}/P{P}")
+        assert np.array_equal(bits(ub.decode("mfma", P), dtype), bits(got, dtype))
 
 
 _GROUPINGS = [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1)]

@@ -33,25 +33,32 @@ def _lengths(S, width, P, seed):
     return [int(x) for x in edges + list(rest) if 1 <= int(x) <= width][:S]
 
 
-# (Hq, Hkv, S, table tokens, P) and the partitions per workgroup the library picks
+# (Hq, Hkv, S, table tokens, P, head dim) and the partitions per workgroup the library picks
 SHAPES = [
-    (32, 8, 64, 1664, 128),    # 4 heads per workgroup, 13 partitions -> 4 per workgroup
-    (32, 8, 64, 1664, 256),    # 7 partitions -> 2 per workgroup
-    (32, 8, 64, 1664, 384),    # 5 partitions -> 1 per workgroup (the grid would be too small)
-    (64, 8, 64, 1664, 128),    # 8 heads per workgroup -> 2 (at most 2 with 8 heads)
-    (32, 2, 128, 3712, 128),   # 16 heads per workgroup -> 1
+    (32, 8, 64, 1664, 128, 128),    # 4 heads per workgroup, 13 partitions -> 4 per workgroup
+    (32, 8, 64, 1664, 256, 128),    # 7 partitions -> 2 per workgroup
+    (32, 8, 64, 1664, 384, 128),    # 5 partitions -> 1 per workgroup (the grid would be too small)
+    (64, 8, 64, 1664, 128, 128),    # 8 heads per workgroup -> 2 (LDS slots for 2)
+    (32, 2, 128, 3712, 128, 128),   # 16 heads per workgroup -> 1
+    (32, 8, 64, 1664, 128, 64),     # head dim 64, 4 heads -> 4
+    (64, 8, 64, 1664, 128, 64),     # head dim 64, 8 heads -> 4
+    (32, 8, 64, 1664, 128, 256),    # head dim 256, 4 heads -> 2
 ]
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8"])
-@pytest.mark.parametrize("Hq,Hkv,S,width,P", SHAPES)
-def test_partition_groups(Hq, Hkv, S, width, P, kv):
+# the 8-bit matrix-core kernel is built for head dim 128 only
+CASES = [(*shape, kv) for shape in SHAPES for kv in ("bf16", "f16", "fp8")
+         if kv != "fp8" or shape[5] == 128]
+
+
+@pytest.mark.parametrize("Hq,Hkv,S,width,P,D,kv", CASES)
+def test_partition_groups(Hq, Hkv, S, width, P, D, kv):
     import torch
     dev = need_gpu()
     dtype = "f16" if kv == "f16" else "bf16"
     lens = _lengths(S, width, P, seed=Hq * 1000 + P)
     S = len(lens)
-    spec = W.CaseSpec("pgroups", 700 + P + Hq, S, Hq, Hkv, 128, dtype, 16, ("fixed", lens),
+    spec = W.CaseSpec("pgroups", 700 + P + Hq + D, S, Hq, Hkv, D, dtype, 16, ("fixed", lens),
                       new_tokens=("free", 0), max_blocks_per_seq=width // 16,
                       kv_dtype="fp8" if kv == "fp8" else None)
     case = W.build_case(spec)
@@ -64,7 +71,7 @@ def test_partition_groups(Hq, Hkv, S, width, P, kv):
     say(f"partition groups {kv}: S={S} Hq={Hq} Hkv={Hkv} width={width} P={P}")
 
     def run(rows):
-        out = torch.empty((len(rows), Hq, 128), dtype=q.dtype, device=dev)
+        out = torch.empty((len(rows), Hq, D), dtype=q.dtype, device=dev)
         idx = torch.tensor(rows, dtype=torch.int64, device=dev)
         qs, bts, cls = q.index_select(0, idx), bt.index_select(0, idx), cl.index_select(0, idx)
         if kv == "fp8":
