@@ -325,6 +325,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   // an even index: settling at the top of each pair, of each block and before a lone last chunk
   // is enough.
   int pending = -1;
+  int left = Q, kpart = 0;   // this wave's chunks left in partition p0 + kpart
   auto settle = [&]() {
     if (pending >= 0) {
       flush(pending);
@@ -428,9 +429,11 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
       acc[e] = M::mma16(phi, bv, acc[e]);
       acc[e] = M::mma16(plo, bv, acc[e]);
     }
-    if (np_wg > 1) {
-      const int j = (ch - ch_begin) >> 2;   // this wave's chunk index in the workgroup's run
-      if ((j + 1) % Q == 0 && (j + 1) / Q < np_wg) pending = (j + 1) / Q - 1;
+    // a countdown, not a division by the runtime Q: full partitions hold Q chunks per wave
+    if (np_wg > 1 && --left == 0) {
+      left = Q;
+      if (kpart < np_wg - 1) pending = kpart;
+      ++kpart;
     }
   };
 
