@@ -584,7 +584,8 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--only", default="",
                     help="time only these detail legs (comma-separated: a decode workload, "
-                         "prefill_llama7b, prefill_gqa, swap_blocks, device_engine) and print them")
+                         "prefill_llama7b, prefill_gqa, swap_blocks, device_engine, read_ceiling) "
+                         "and print them")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -612,6 +613,8 @@ def main(argv=None):
                 res[leg] = measure_swap(dev, args.steps)
             elif leg == "device_engine":
                 res[leg] = measure_device_engine(dev, args.steps, args.warmup)
+            elif leg == "read_ceiling":
+                res[leg] = read_ceiling(dev, args.steps)
             elif leg in W.CONFIGS:
                 c2, st2, ms2, k2, _, _ = run_workload(leg, dev, args.steps, args.warmup, args.kernel)
                 res[leg] = {"ms_per_step": round(ms2, 4), "decode_kernel_ms": round(k2, 4),
