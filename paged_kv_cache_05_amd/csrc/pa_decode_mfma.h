@@ -93,12 +93,21 @@ template <> struct Mfma<DT::F16> {
 constexpr float kLazy = 8.0f;   // running-max slack (log2 units): probabilities < 256
 
 // Four E4M3 codes (one word) as four 16-bit values of the query type, two words.  Exact: every
-// E4M3 value (3 mantissa bits, 2^-9 .. 448) is representable in bfloat16 and in fp16.
+// E4M3 value (3 mantissa bits, 2^-9 .. 448) is representable in bfloat16 and in fp16.  One
+// scaled packed conversion per two codes, with scale 1 (gfx950 converts E4M3 pairs straight to
+// 16-bit pairs; checked bit for bit against the convert-to-fp32-then-round path on every pair
+// of codes, NaN included).
 template <class M>
 __device__ __forceinline__ uint2 fp8x4_to_16bit(uint32_t w) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return make_uint2(M::pack2(lo[0], lo[1]), M::pack2(hi[0], hi[1]));
+  if constexpr (std::is_same_v<M, Mfma<DT::BF16>>) {
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+  } else {
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+  }
 }
 
 // 8-byte K/V load (rows of an 8-bit cache), streaming or cache-allocating like load_kv

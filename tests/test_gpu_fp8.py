@@ -300,3 +300,36 @@ def test_decode_fp8_two_launches_equal_one(heads):
         torch.cuda.synchronize()
         assert np.array_equal(W.from_torch(one, "bf16").view(np.uint16),
                               W.from_torch(two, "bf16").view(np.uint16)), P
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 4, 4), ("f16", 4, 4), ("bf16", 16, 4),
+                                          ("f16", 16, 4)])
+def test_decode_fp8_every_code_one_token(dtype, Hq, Hkv):
+    """Every finite E4M3 code as a value, in one-token contexts: the output is that token's
+    dequantized V row, exactly (a code times the power-of-two value scale is exact in both
+    16-bit types), on the vector-ALU kernel (G = 1) and the matrix-core kernel (G = 4)."""
+    import torch
+    dev = need_gpu()
+    S = 8
+    case = W.build_case(_spec(dtype, 16, Hq, Hkv, [1] * S, seed=4242))
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 finite
+    vc = case.value_cache.copy()
+    D = case.spec.head_dim
+    for s in range(S):
+        blk = int(case.block_tables[s][0])
+        for g in range(Hkv):
+            start = ((s * Hkv + g) * D) % len(codes)
+            vc[blk, g, 0, :] = np.resize(np.roll(codes, -start), D)
+    say(f"decode_fp8 every code {dtype} Hq{Hq} Hkv{Hkv}")
+    case.value_cache = vc
+    q, kc, vct, bt, cl = _upload(case, dev)
+    out = torch.empty_like(q)
+    ops.decode_fp8(out, q, kc, vct, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE))
+    torch.cuda.synchronize()
+    got = W.from_torch(out, dtype)
+    ref = oracle.f64_to_storage(_oracle(case), dtype)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+    seen = set()
+    for s in range(S):
+        seen.update(vc[int(case.block_tables[s][0]), :, 0, :].ravel().tolist())
+    assert seen == set(codes.tolist())
