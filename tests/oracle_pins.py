@@ -246,17 +246,20 @@ def pin_golden_page_count(O):
 
 def pin_fragmentation(O):
     """Waste is under one block per sequence: utilisation >= sum(n) / (sum(n) + S*(bs-1)),
-    checked against a brute-force count of the slots a block manager reserves."""
+    checked against a brute-force count of the slots reserved when tokens arrive one at a time
+    and a block is taken only when the sequence's last block is full (jsqmd page, paged-memory
+    workflow; the reading that a new token fills the next free slot)."""
     rng = np.random.default_rng(9)
     for bs in (16, 32):
         lens = rng.integers(1, 300, size=40)
-        bm = BlockManager(4000, bs, seed=1)
-        sids = []
+        reserved = 0
         for n in lens:
-            sid = bm.new_sequence()
-            bm.append_tokens(sid, int(n))
-            sids.append(sid)
-        reserved = sum(len(bm.table(s)) for s in sids) * bs
+            blocks, fill = 0, bs
+            for _ in range(int(n)):
+                if fill == bs:
+                    blocks, fill = blocks + 1, 0
+                fill += 1
+            reserved += blocks * bs
         u = O.slot_utilization(lens, bs)
         assert abs(u - lens.sum() / reserved) <= 1e-15
         assert u >= lens.sum() / (lens.sum() + len(lens) * (bs - 1))
@@ -738,24 +741,25 @@ def pin_fnv_vectors(O):
 def pin_block_hashes(O):
     """Block j's hash depends on exactly tokens 0 .. (j+1)bs-1: sequences with a common prefix
     share the hashes of the blocks inside it and differ afterwards; changing one token changes
-    its block's hash and every later one only; blocks that are not full hash to 0; hashes
-    chain h_j = FNV(h_{j-1} || g_j) (checked for two blocks by hand)."""
+    its block's hash and every later one only; blocks that are not full hash to 0; the chain
+    is order-sensitive (two full blocks swapped give different hashes from the first block on);
+    no two of 2000 random single-block prefixes collide."""
     rng = np.random.default_rng(9)
     bs, T = 4, 24
     base = rng.integers(0, 50000, size=T, dtype=np.int32)
-    tok = np.stack([base, base, base, base])
+    tok = np.stack([base, base, base, base, base])
     tok[1, 13] += 1                       # differs in block 3
     tok[2, 0] += 7                        # differs from the start
-    lens = np.array([24, 24, 24, 10], np.int32)
+    tok[4, :4], tok[4, 4:8] = base[4:8], base[:4]   # blocks 0 and 1 swapped
+    lens = np.array([24, 24, 24, 10, 24], np.int32)
     h = O.block_hashes_ref(tok, lens, bs)
     assert np.array_equal(h[1, :3], h[0, :3]) and np.all(h[1, 3:] != h[0, 3:])
     assert np.all(h[2] != h[0])
     assert np.array_equal(h[3, :2], h[0, :2]) and np.all(h[3, 2:] == 0)
-    g0 = O.fnv1a64(base[:4].astype("<i4").tobytes())
-    h0 = O.fnv1a64((0).to_bytes(8, "little") + g0.to_bytes(8, "little"))
-    g1 = O.fnv1a64(base[4:8].astype("<i4").tobytes())
-    h1 = O.fnv1a64(h0.to_bytes(8, "little") + g1.to_bytes(8, "little"))
-    assert int(h[0, 0]) == h0 and int(h[0, 1]) == h1
+    assert np.all(h[4] != h[0])
+    many = rng.integers(0, 1 << 20, size=(2000, bs), dtype=np.int32)
+    hm = O.block_hashes_ref(many, np.full(2000, bs, np.int32), bs)[:, 0]
+    assert len(set(hm.tolist())) == 2000 and np.all(hm != 0)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
