@@ -19,6 +19,7 @@ from .pa_oracle import (  # noqa: F401
     free_seqs_ref,
     fp8_e4m3_to_f64,
     kv_bytes_per_token,
+    prefill_fp8_ref,
     prefill_ref,
     quantize_fp8,
     num_blocks_for,

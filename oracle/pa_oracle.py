@@ -404,6 +404,16 @@ def decode_fp8_ref(query, key_cache, value_cache, block_tables, context_lens, bl
     return decode_ref(qf, kc, vc, block_tables, context_lens, block_size, scale, "f64")
 
 
+def prefill_fp8_ref(query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+                    block_size, scale, dtype: str, k_scale, v_scale) -> np.ndarray:
+    """Chunked prefill over an 8-bit cache: prefill_ref on the dequantized pools (codes times
+    each pool's scale, exactly); ``dtype`` is the query's type."""
+    keys = dequantize_fp8(key_cache, k_scale)
+    values = dequantize_fp8(value_cache, v_scale)
+    return prefill_ref(storage_to_f64(query, dtype), keys, values, block_tables, query_start_loc,
+                       context_lens, block_size, scale, "f64")
+
+
 # ---------------------------------------------------------------------------------------
 # block engine: append with copy-on-write, fork, free, prefix-block hashes
 # ---------------------------------------------------------------------------------------

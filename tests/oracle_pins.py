@@ -633,6 +633,45 @@ def pin_fp8_cache_and_decode(O):
         assert np.max(np.abs(out[s] - ref)) <= 1e-12, s
 
 
+def pin_fp8_prefill(O):
+    """Prefill over 8-bit pools: whole prompts equal torch's float64 causal SDPA
+    (``is_causal=True``) on the contiguous K/V decoded by torch's float8_e4m3fn times each
+    pool's scale, with GQA; chunks on a cached prefix equal, row by row, an 8-bit decode of that
+    row over its context (decode_fp8_ref is pinned above)."""
+    rng = np.random.default_rng(8)
+    ks, vs = np.float32(0.05), np.float32(0.25)
+    for prefix, chunk, seed in (((0, 0, 0), (1, 19, 33), 70), ((0, 7, 40), (5, 9, 16), 71)):
+        c = _pcase(S=3, Hq=4, Hkv=2, d=16, dtype="bf16", bs=16, prefix=prefix, chunk=chunk, seed=seed)
+        shape = c.pool.key_cache.shape
+        kc = rng.integers(0, 0x7F, size=shape, dtype=np.uint8) | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+        vc = rng.integers(0, 0x7F, size=shape, dtype=np.uint8) | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+        out = O.prefill_fp8_ref(c.query, kc, vc, c.pool.block_tables, c.query_start_loc,
+                                c.context_lens, c.block_size, c.scale, "bf16", ks, vs)
+        q = O.storage_to_f64(c.query, "bf16")
+        for s in range(3):
+            q0, q1 = int(c.query_start_loc[s]), int(c.query_start_loc[s + 1])
+            n = int(c.context_lens[s])
+            nb = -(-n // c.block_size)
+            blocks = c.pool.block_tables[s][:nb]
+            Kc = np.concatenate([kc[b] for b in blocks], axis=1)[:, :n]       # [Hkv, n, d] codes
+            Vc = np.concatenate([vc[b] for b in blocks], axis=1)[:, :n]
+            K = _torch_fp8_values(Kc) * float(ks)
+            V = _torch_fp8_values(Vc) * float(vs)
+            if prefix[s] == 0:
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(np.ascontiguousarray(q[q0:q1].transpose(1, 0, 2)))[None],
+                    torch.from_numpy(np.ascontiguousarray(K))[None],
+                    torch.from_numpy(np.ascontiguousarray(V))[None],
+                    is_causal=True, scale=float(c.scale), enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+                assert np.max(np.abs(out[q0:q1] - ref)) <= 1e-12, ("whole prompt", s)
+            for i in range(q1 - q0):
+                pos = n - (q1 - q0) + i
+                row = O.decode_fp8_ref(c.query[q0 + i:q0 + i + 1], kc, vc,
+                                       c.pool.block_tables[s:s + 1], np.array([pos + 1], np.int32),
+                                       c.block_size, c.scale, "bf16", ks, vs)
+                assert np.max(np.abs(out[q0 + i] - row[0])) <= 1e-12, ("row", s, i)
+
+
 # ---------------------------------------------------------------------------------------
 # block engine and prefix hashes
 # ---------------------------------------------------------------------------------------

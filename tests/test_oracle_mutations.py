@@ -68,6 +68,9 @@ MUTATIONS = [
     ("fp8 no saturation", "    y = np.clip(y, np.float32(-FP8_MAX), np.float32(FP8_MAX))\n", ""),
     ("fp8 scale multiplies", "inv = np.float32(1.0) / np.float32(scale)", "inv = np.float32(scale)"),
     ("fp8 value scale for keys", "    kc = dequantize_fp8(key_cache, k_scale)", "    kc = dequantize_fp8(key_cache, v_scale)"),
+    ("fp8 prefill key scale", "    keys = dequantize_fp8(key_cache, k_scale)", "    keys = dequantize_fp8(key_cache, v_scale)"),
+    ("fp8 prefill values from keys", "    values = dequantize_fp8(value_cache, v_scale)",
+     "    values = dequantize_fp8(key_cache, v_scale)"),
     ("CoW on any reference", "            if refs[block] > 1:", "            if refs[block] >= 1:"),
     ("CoW keeps the old reference", "                refs[block] -= 1\n", "                pass\n"),
     ("fresh block unreferenced", "            tables[s, j] = new\n            refs[new] = 1\n", "            tables[s, j] = new\n"),
