@@ -335,8 +335,11 @@ def build_case(spec: CaseSpec, *, device=None, poison=False, table_fill=-1,
             if not free_mode and len(slots):
                 # the step's own slots are written by reshape_and_cache before decode reads them
                 dead[slots] = True
+            # slot b*bs + o is pool[b, :, o, :]; index the pool itself (a reshaped
+            # transpose would be a copy, and writing into it would leave the pool clean)
+            db, do = np.divmod(np.flatnonzero(dead), bs)
             for pool in (kc, vc):
-                _slot_view(pool)[:, dead, :] = nan_storage(pdt)
+                pool[db, :, do, :] = nan_storage(pdt)
         case.key_cache, case.value_cache = kc, vc
         if keep_contiguous and not spec.shared_prefix:
             case.contiguous = []

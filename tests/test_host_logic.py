@@ -113,3 +113,22 @@ def test_gpu_free_case_tables_are_in_range():
             assert (row >= 0).all() and (row < c.num_blocks).all()
         flat = np.concatenate([c.block_tables[s, : nb[s]] for s in range(8)])
         assert len(set(flat.tolist())) == len(flat)
+
+
+@pytest.mark.parametrize("kv", [None, "fp8"])
+def test_poison_marks_every_dead_slot(kv):
+    """A poisoned pool holds the NaN pattern in exactly the slots no live token uses, in every
+    head and element, and the live rows are unchanged from the clean pool."""
+    spec = W.CaseSpec("p", 5, 3, 4, 2, 64, "bf16", 16, ("fixed", [100, 128, 37]),
+                      new_tokens=("free", 0), kv_dtype=kv)
+    clean, dirty = W.build_case(spec), W.build_case(spec, poison=True)
+    nan = 0x7F if kv else 0x7FC0
+    for a, b in ((clean.key_cache, dirty.key_cache), (clean.value_cache, dirty.value_cache)):
+        nb, h, bs, d = b.shape
+        slots = b.transpose(1, 0, 2, 3).reshape(h, nb * bs, d)
+        dead = np.ones(nb * bs, bool)
+        dead[dirty.live_slots] = False
+        assert np.all(slots[:, dead, :] == nan)
+        assert not np.any(np.all(slots[:, ~dead, :] == nan, axis=(0, 2)))
+        live = a.transpose(1, 0, 2, 3).reshape(h, nb * bs, d)[:, ~dead, :]
+        assert np.array_equal(live, slots[:, ~dead, :])
