@@ -461,10 +461,17 @@ def measure_prefill(dev, name, steps, warmup):
     res = {"flops_per_launch": flops, "num_seqs": sp.num_seqs, "num_heads": sp.num_heads,
            "num_kv_heads": sp.num_kv_heads, "chunk": _lengths_str(sp.chunk_lengths),
            "cached_prefix": str(sp.prefix_lengths), "key_split_workspace_bytes": need}
+    if sp.kv_dtype == "fp8":
+        res["kv_cache"] = "E4M3, both pool scales 1/64"
     for mode, bf16_p in (("p16", False), ("p_bf16", True)):
         def run():
-            ops.prefill(out, q, case.pool.key_cache, case.pool.value_cache, bt, qsl, cl,
-                        float(case.scale), case.max_query_len, bf16_p=bf16_p, workspace=ws)
+            if sp.kv_dtype == "fp8":
+                ops.prefill_fp8(out, q, case.pool.key_cache, case.pool.value_cache, bt, qsl, cl,
+                                float(case.scale), case.max_query_len, W.FP8_DRAW_SCALE,
+                                W.FP8_DRAW_SCALE, bf16_p=bf16_p, workspace=ws)
+            else:
+                ops.prefill(out, q, case.pool.key_cache, case.pool.value_cache, bt, qsl, cl,
+                            float(case.scale), case.max_query_len, bf16_p=bf16_p, workspace=ws)
         # warm up for at least `warmup` launches and 0.2 s: the first launches after the pools
         # are drawn run ~10% slow (measured), longer than ten 0.5 ms launches last
         t_end = time.perf_counter() + 0.2
@@ -584,7 +591,8 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--only", default="",
                     help="time only these detail legs (comma-separated: a decode workload, "
-                         "prefill_llama7b, prefill_gqa, swap_blocks, device_engine, read_ceiling) "
+                         "prefill_llama7b, prefill_gqa, prefill_llama7b_fp8, swap_blocks, "
+                         "device_engine, read_ceiling) "
                          "and print them")
     args = ap.parse_args(argv)
 
@@ -722,7 +730,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         detail["read_ceiling"] = read_ceiling(dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
-        for pname in ("prefill_llama7b", "prefill_gqa"):
+        for pname in ("prefill_llama7b", "prefill_gqa", "prefill_llama7b_fp8"):
             detail[pname] = measure_prefill(dev, pname, args.steps, args.warmup)
         torch.cuda.empty_cache()
         detail["shared_prefix_device_engine"] = measure_device_engine(dev, args.steps, args.warmup)

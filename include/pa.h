@@ -389,6 +389,26 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
                                    void* stream);
 
 /*
+ * pa_prefill_fp8 — pa_prefill_ex over E4M3 pools: the result is prefill attention over
+ * K = code * k_scale and V = code * v_scale (exact values).  query and out are dtype (PA_F16 or
+ * PA_BF16); pools are uint8 as above.  The codes are widened exactly to dtype as each key/value
+ * tile is staged, so the products, the probability precision (flags: PA_PREFILL_BF16_P) and the
+ * key splits (kv_split, workspace: pa_prefill_workspace_bytes with the same sizes) are
+ * pa_prefill_ex's; k_scale is folded into the score scale (one rounding of scale * k_scale) and
+ * v_scale into the final normalisation.  Supported shapes as pa_prefill.  Errors as
+ * pa_prefill_ex, plus PA_ERR_BAD_SHAPE for a scale that is not finite and > 0.
+ */
+pa_status pa_prefill_fp8(void* out, const void* query, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* query_start_loc, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                         float scale, pa_dtype dtype, float k_scale, float v_scale,
+                         int32_t kv_split, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, void* stream);
+
+/*
  * Block engine on the device.  The KV cache manager maps each sequence's logical blocks to
  * physical ones, allocates on demand and reclaims (xasun.com summary §二, block-engine item);
  * shared blocks carry reference counts and are copied before a sharer writes (same page,

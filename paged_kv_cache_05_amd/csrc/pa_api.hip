@@ -442,14 +442,16 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t 
   return pl.ws_bytes;
 }
 
-pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
-                        const void* value_cache, const int32_t* block_tables,
-                        const int32_t* query_start_loc, const int32_t* context_lens,
-                        int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
-                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
-                        float scale, pa_dtype dtype, int32_t kv_split, void* workspace,
-                        size_t workspace_bytes, uint32_t flags, void* stream) {
+// pa_prefill_ex and pa_prefill_fp8: kv8 selects E4M3 pools with scales k_scale and v_scale
+static pa_status prefill_call(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                              float scale, pa_dtype dtype, bool kv8, float k_scale, float v_scale,
+                              int32_t kv_split, void* workspace, size_t workspace_bytes,
+                              uint32_t flags, void* stream) {
   DT dt;
   if (!dtype_of(dtype, &dt)) return PA_ERR_UNSUPPORTED;
   pa_status st = check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
@@ -468,6 +470,8 @@ pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
       !context_lens)
     return PA_ERR_NULL_PTR;
   if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (kv8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return PA_ERR_BAD_SHAPE;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return PA_ERR_WORKSPACE;
   const int G = num_heads / num_kv_heads;
   const long grid = (long)num_seqs * num_kv_heads * pl.row_tiles * pl.kv_splits;
@@ -492,7 +496,11 @@ pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
   // The kernel takes the row max on raw scores, which needs a positive multiplier: a negative
   // scale flips the query signs instead (exact), and 0 becomes the smallest normal float
   // (every score then rounds to a zero exponent, as scale 0 requires).
-  p.scale_log2 = std::max(std::fabs(scale) * 1.4426950408889634f, 1.17549435e-38f);
+  // An E4M3 key pool's scale multiplies every score: folded in here (exact up to the one
+  // rounding of the product).
+  const float kmul = kv8 ? k_scale : 1.0f;
+  p.scale_log2 = std::max(std::fabs(scale) * kmul * 1.4426950408889634f, 1.17549435e-38f);
+  p.v_scale = kv8 ? v_scale : 1.0f;
   p.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
   p.kv_splits = pl.kv_splits;
   p.split_tiles = pl.split_tiles;
@@ -504,7 +512,7 @@ pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
   const bool split_p = !(dt == DT::BF16 && (flags & PA_PREFILL_BF16_P));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = pa::launch_prefill_mfma(dt, block_size, split_p, p, (int)grid, s);
+  hipError_t e = pa::launch_prefill_mfma(dt, kv8, block_size, split_p, p, (int)grid, s);
   if (e != hipSuccess || pl.kv_splits == 1) return launch_status(e);
   // combine the split partials: every query token is a "sequence" whose context is its
   // position + 1, partitioned by the split length
@@ -520,6 +528,35 @@ pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
   m.partition = pl.split_tiles * 64;
   m.max_parts = pl.kv_splits;
   return launch_status(pa::launch_merge(dt, head_dim, m, s));
+}
+
+pa_status pa_prefill_ex(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        const int32_t* query_start_loc, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                        float scale, pa_dtype dtype, int32_t kv_split, void* workspace,
+                        size_t workspace_bytes, uint32_t flags, void* stream) {
+  return prefill_call(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, max_query_len, scale, dtype,
+                      false, 1.0f, 1.0f, kv_split, workspace, workspace_bytes, flags, stream);
+}
+
+pa_status pa_prefill_fp8(void* out, const void* query, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* query_start_loc, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                         float scale, pa_dtype dtype, float k_scale, float v_scale,
+                         int32_t kv_split, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, void* stream) {
+  return prefill_call(out, query, key_cache, value_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_tokens, num_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, max_query_len, scale, dtype,
+                      true, k_scale, v_scale, kv_split, workspace, workspace_bytes, flags, stream);
 }
 
 pa_status pa_prefill(void* out, const void* query, const void* key_cache, const void* value_cache,

@@ -58,6 +58,13 @@ template <> struct Mma<DT::BF16> {
   }
   static constexpr uint32_t kOnes = 0x3F803F80u;   // two bfloat16 ones
   __device__ __forceinline__ static uint32_t bits(float f) { return bf16_bits(f); }
+  // E4M3 codes 0,1 (or 2,3) of a word as two bfloat16 values (exact), one instruction
+  __device__ __forceinline__ static uint32_t fp8_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  }
+  __device__ __forceinline__ static uint32_t fp8_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  }
   // two values, nearest-even, in one v_cvt_pk_bf16_f32
   __device__ __forceinline__ static uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
@@ -70,6 +77,12 @@ template <> struct Mma<DT::F16> {
   }
   static constexpr uint32_t kOnes = 0x3C003C00u;   // two fp16 ones
   __device__ __forceinline__ static uint32_t bits(float f) { return f16_bits(f); }
+  __device__ __forceinline__ static uint32_t fp8_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  }
+  __device__ __forceinline__ static uint32_t fp8_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  }
   __device__ __forceinline__ static uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
   }
@@ -84,9 +97,15 @@ constexpr float kLazy = 8.0f;    // running-max slack (log2 units): probabilitie
 
 __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
-template <DT dt, int BS, bool SPLIT_P>
+template <DT dt, int BS, bool SPLIT_P, bool K8>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParams p) {
   using M = Mma<dt>;
+  // K8: E4M3 pools (128-byte token rows); the codes are widened to dt when a tile is stored in
+  // LDS, so the products below are the 16-bit ones.  The key scale is folded into scale_log2 by
+  // the host, the value scale into the final normalisation.
+  constexpr int CROW = K8 ? kD : kRow;      // bytes of one cached token row
+  constexpr int CPIECE = K8 ? 8 : 16;       // bytes of a row one loader thread moves
+  using Raw = std::conditional_t<K8, uint2, uint4>;
   static_assert(BS % 8 == 0, "a thread's 4 tokens must sit in one block");
   __shared__ uint4 s_k[2][kTile * 16];
   __shared__ uint4 s_v[2][kD * 8];
@@ -196,33 +215,39 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   const int tg = ((p16 >> 1) & 3) | ((l16 >> 3) << 2) | ((p16 >> 3) << 3);
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int nb_live = (n + BS - 1) / BS;
-  const size_t head_off = (size_t)kvh * BS * kRow;
-  const size_t blk_stride = (size_t)p.num_kv_heads * BS * kRow;
+  const size_t head_off = (size_t)kvh * BS * CROW;
+  const size_t blk_stride = (size_t)p.num_kv_heads * BS * CROW;
   auto entry = [&](int tile) -> int {
     const int page = (tile * kTile + 4 * tg) / BS;
     return (tile < k_end && page < nb_live) ? table[page] : -1;
   };
-  uint4 kr[4], vr[4];
+  Raw kr[4], vr[4];
   auto issue = [&](int tile, int ent) {
     const int t0 = tile * kTile + 4 * tg;
     // An id outside the pool (a broken table) is replaced by block 0, so no access leaves the
     // pools; slots past the context are never read.
     const size_t off = (size_t)((unsigned)ent < (unsigned)p.num_blocks ? ent : 0) * blk_stride +
-                       head_off + (size_t)(t0 % BS) * kRow + dc * 16;
+                       head_off + (size_t)(t0 % BS) * CROW + dc * CPIECE;
     const char* kp = (const char*)p.kc + off;
     const char* vp = (const char*)p.vc + off;
     if (t0 + 3 < n) {   // the usual case: four live rows, unconditional loads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kr[i] = *reinterpret_cast<const uint4*>(kp + i * kRow);
-        vr[i] = *reinterpret_cast<const uint4*>(vp + i * kRow);
+        kr[i] = *reinterpret_cast<const Raw*>(kp + i * CROW);
+        vr[i] = *reinterpret_cast<const Raw*>(vp + i * CROW);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool live = t0 + i < n;
-        kr[i] = live ? *reinterpret_cast<const uint4*>(kp + i * kRow) : make_uint4(0, 0, 0, 0);
-        vr[i] = live ? *reinterpret_cast<const uint4*>(vp + i * kRow) : make_uint4(0, 0, 0, 0);
+        Raw zk, zv;
+        if constexpr (K8) {
+          zk = zv = make_uint2(0, 0);
+        } else {
+          zk = zv = make_uint4(0, 0, 0, 0);
+        }
+        kr[i] = live ? *reinterpret_cast<const Raw*>(kp + i * CROW) : zk;
+        vr[i] = live ? *reinterpret_cast<const Raw*>(vp + i * CROW) : zv;
       }
     }
   };
@@ -230,17 +255,31 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   // so the 8 tokens one MFMA lane needs (4g+i of 16-token blocks 2h and 2h+1) are contiguous.
   const int v_chunk = 4 * (tg >> 3) + (tg & 3);
   const int v_half = (tg >> 2) & 1;
+  // a loaded row piece as 8 values of dt (16 bytes): as loaded, or 8 E4M3 codes widened
+  auto widen = [](const Raw& r) -> uint4 {
+    if constexpr (K8) {
+      return make_uint4(M::fp8_lo(r.x), M::fp8_hi(r.x), M::fp8_lo(r.y), M::fp8_hi(r.y));
+    } else {
+      return r;
+    }
+  };
   auto stash = [&](int buf) {
+    uint4 kw[4], vw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kw[i] = widen(kr[i]);
+      vw[i] = widen(vr[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * tg + i;
-      s_k[buf][t * 16 + (dc ^ (t & 15))] = kr[i];
+      s_k[buf][t * 16 + (dc ^ (t & 15))] = kw[i];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = 8 * dc + e;
       char* dst = reinterpret_cast<char*>(&s_v[buf][d * 8 + (v_chunk ^ vswz(d))]) + 8 * v_half;
-      *reinterpret_cast<uint2*>(dst) = tile_column(vr, e);
+      *reinterpret_cast<uint2*>(dst) = tile_column(vw, e);
     }
   };
 
@@ -403,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   const int split_len = p.split_tiles * kTile;
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const float inv = 1.0f / l_acc[c2][0];
+    const float inv = p.v_scale / l_acc[c2][0];   // 1 for 16-bit pools
     const int r = wrow0 + 16 * c2 + lr;
     const int np = KS == 1 ? 1 : (lim[c2] + split_len) / split_len;   // splits holding its keys
     if (r < rows && np == 1 && ks == 0) {
@@ -429,33 +468,38 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(const PrefillParam
   }
 }
 
-template <DT dt, int BS, bool SPLIT>
+template <DT dt, int BS, bool SPLIT, bool K8>
 hipError_t go(const PrefillParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<dt, BS, SPLIT>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<dt, BS, SPLIT, K8>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(DT dt, int block_size, bool split_p, const PrefillParams& p,
-                               int grid, hipStream_t st) {
-  auto by_bs = [&](auto dt_tag, auto split_tag) -> hipError_t {
+hipError_t launch_prefill_mfma(DT dt, bool kv8, int block_size, bool split_p,
+                               const PrefillParams& p, int grid, hipStream_t st) {
+  auto by_bs = [&](auto dt_tag, auto split_tag, auto k8_tag) -> hipError_t {
     constexpr DT T = decltype(dt_tag)::value;
     constexpr bool SP = decltype(split_tag)::value;
+    constexpr bool K8 = decltype(k8_tag)::value;
     switch (block_size) {
-      case 8: return go<T, 8, SP>(p, grid, st);
-      case 16: return go<T, 16, SP>(p, grid, st);
-      case 32: return go<T, 32, SP>(p, grid, st);
-      case 64: return go<T, 64, SP>(p, grid, st);
-      case 128: return go<T, 128, SP>(p, grid, st);
+      case 8: return go<T, 8, SP, K8>(p, grid, st);
+      case 16: return go<T, 16, SP, K8>(p, grid, st);
+      case 32: return go<T, 32, SP, K8>(p, grid, st);
+      case 64: return go<T, 64, SP, K8>(p, grid, st);
+      case 128: return go<T, 128, SP, K8>(p, grid, st);
     }
     return hipErrorInvalidValue;
+  };
+  auto by_kv = [&](auto dt_tag, auto split_tag) -> hipError_t {
+    return kv8 ? by_bs(dt_tag, split_tag, std::true_type{})
+               : by_bs(dt_tag, split_tag, std::false_type{});
   };
   using BF = std::integral_constant<DT, DT::BF16>;
   using HF = std::integral_constant<DT, DT::F16>;
   if (dt == DT::BF16)
-    return split_p ? by_bs(BF{}, std::true_type{}) : by_bs(BF{}, std::false_type{});
-  if (dt == DT::F16) return by_bs(HF{}, std::false_type{});
+    return split_p ? by_kv(BF{}, std::true_type{}) : by_kv(BF{}, std::false_type{});
+  if (dt == DT::F16) return by_kv(HF{}, std::false_type{});
   return hipErrorInvalidValue;
 }
 

@@ -61,6 +61,8 @@ _SIGNATURES = {
                                                                  _c_float, _c_int, _p, _c_size,
                                                                  ctypes.c_uint32, _p]),
     "pa_read_tiles": (_c_int, [_p, ctypes.c_int64, _c_int, _p, _c_int, _p, _p]),
+    "pa_prefill_fp8": (_c_int, [_p] * 7 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float,
+                                                       _c_int, _p, _c_size, ctypes.c_uint32, _p]),
 }
 
 
@@ -408,6 +410,36 @@ def decode_fp8_partitions(out, query, key_cache, value_cache, block_tables, cont
                                            _ptr(workspace), wsb,
                                            PA_DECODE_SHARED_BLOCKS if shared_blocks else 0,
                                            _stream(dev, stream)), "pa_decode_fp8_partitions")
+
+
+def prefill_fp8(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens,
+                scale, max_query_len, k_scale, v_scale, *, bf16_p=False, kv_split=0,
+                workspace=None, stream=None):
+    """pa_prefill_fp8: ``prefill`` over E4M3 pools (codes times k_scale / v_scale)."""
+    import torch
+    dev = _dev(out, query, key_cache, value_cache, block_tables, query_start_loc, context_lens)
+    T, Hq, D = query.shape
+    NB, Hkv, BS, D2 = _fp8_pools(key_cache, value_cache)
+    S = context_lens.shape[0]
+    if D2 != D or tuple(out.shape) != (T, Hq, D) or out.dtype != query.dtype:
+        raise ValueError("out must match the query; pools [num_blocks, num_kv_heads, block_size, head_dim]")
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start_loc.dtype != torch.int32):
+        raise TypeError("block_tables, query_start_loc and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start_loc.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and query_start_loc [S + 1]")
+    maxb = block_tables.shape[1]
+    need = prefill_workspace_bytes(S, T, Hq, Hkv, D, BS, maxb, int(max_query_len), int(kv_split))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(load().pa_prefill_fp8(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                 _ptr(block_tables), _ptr(query_start_loc), _ptr(context_lens), S,
+                                 T, Hq, Hkv, D, BS, NB, maxb, int(max_query_len), float(scale),
+                                 _dtype_code(query), float(k_scale), float(v_scale), int(kv_split),
+                                 _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                 PA_PREFILL_BF16_P if bf16_p else 0, _stream(dev, stream)),
+           "pa_prefill_fp8")
+    return out
 
 
 # ---------------------------------------------------------------------------------------

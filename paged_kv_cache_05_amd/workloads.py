@@ -437,6 +437,7 @@ class PrefillSpec:
     chunk_lengths: tuple               # new tokens in this chunk
     pool_fill: float = 0.9
     max_blocks_per_seq: int | None = None
+    kv_dtype: str | None = None        # pool element type when it differs ("fp8")
 
 
 PREFILL_CONFIGS = {
@@ -446,6 +447,9 @@ PREFILL_CONFIGS = {
     # grouped-query heads, ragged chunks, long prefixes
     "prefill_gqa": PrefillSpec("prefill_gqa", 7, 8, 32, 8, 128, "bf16", 16,
                                ("uniform", 0, 3000), ("uniform", 1, 700)),
+    # the Llama-7B-shaped chunked prefill over an E4M3 cache
+    "prefill_llama7b_fp8": PrefillSpec("prefill_llama7b_fp8", 6, 32, 32, 32, 128, "bf16", 16,
+                                       ("uniform", 0, 1536), ("fixed", [512] * 32), kv_dtype="fp8"),
 }
 
 
@@ -488,7 +492,8 @@ def build_prefill_case(spec: PrefillSpec, *, device=None, poison=False, table_fi
     pool_spec = CaseSpec(spec.name, int(c_pool.generate_state(1)[0]), S, spec.num_heads,
                          spec.num_kv_heads, spec.head_dim, spec.dtype, spec.block_size,
                          ("fixed", [int(n) for n in ctx]), pool_fill=spec.pool_fill,
-                         new_tokens=("free", 0), max_blocks_per_seq=spec.max_blocks_per_seq)
+                         new_tokens=("free", 0), max_blocks_per_seq=spec.max_blocks_per_seq,
+                         kv_dtype=spec.kv_dtype)
     pool = build_case(pool_spec, device=device, poison=poison, table_fill=table_fill,
                       keep_contiguous=keep_contiguous)
     qsl = np.zeros(S + 1, dtype=np.int32)

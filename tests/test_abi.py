@@ -146,6 +146,33 @@ def _prefill_ex(lib, **kw):
                              a["split"], p(a["ws"]), a["wsb"], a["flags"], None)
 
 
+def _prefill_fp8(lib, **kw):
+    a = dict(out=1, q=1, kc=1, vc=1, bt=1, qsl=1, cl=1, S=4, T=100, Hq=8, Hkv=2, D=128, BS=16,
+             NB=100, maxb=8, maxq=64, scale=0.1, dtype=2, ks=0.5, vs=0.25, split=1024, ws=0,
+             wsb=0, flags=0)
+    a.update(kw)
+    p = lambda v: ctypes.c_void_p(v) if v else None
+    return lib.pa_prefill_fp8(p(a["out"]), p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]),
+                              p(a["qsl"]), p(a["cl"]), a["S"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                              a["BS"], a["NB"], a["maxb"], a["maxq"], a["scale"], a["dtype"],
+                              a["ks"], a["vs"], a["split"], p(a["ws"]), a["wsb"], a["flags"], None)
+
+
+def test_prefill_fp8_argument_errors(lib):
+    """pa_prefill_fp8 checks its arguments like pa_prefill_ex, and its pool scales."""
+    assert _prefill_fp8(lib, ks=0.0) == 2                       # PA_ERR_BAD_SHAPE
+    assert _prefill_fp8(lib, vs=-1.0) == 2
+    assert _prefill_fp8(lib, ks=float("inf")) == 2
+    assert _prefill_fp8(lib, vs=float("nan")) == 2
+    assert _prefill_fp8(lib, out=0) == 1                        # PA_ERR_NULL_PTR
+    assert _prefill_fp8(lib, dtype=0) == 3                      # f32 queries: unsupported
+    assert _prefill_fp8(lib, D=64) == 3
+    assert _prefill_fp8(lib, flags=0x2) == 3
+    assert _prefill_fp8(lib, flags=0x1, out=0) == 1             # bf16 probabilities accepted
+    assert _prefill_fp8(lib, split=512, maxb=64) == 4           # a split needs the workspace
+    assert _prefill_fp8(lib, S=0, out=0) == 0
+
+
 def test_plain_decode_argument_errors(lib):
     """pa_decode (the basic entry) checks its arguments like pa_decode_ex."""
     p = lambda v: ctypes.c_void_p(v) if v else None
