@@ -172,8 +172,9 @@ struct PrefillPlan {
 };
 
 pa_status prefill_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_query_len,
-                       int32_t num_tokens, int32_t kv_split, PrefillPlan* pl) {
+                       int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                       int32_t max_query_len, int32_t num_tokens, int32_t kv_split,
+                       PrefillPlan* pl) {
   if (kv_split < 0 || kv_split % 64 != 0) return PA_ERR_BAD_SHAPE;
   const long G = num_heads / num_kv_heads;
   pl->row_tiles = ((long)max_query_len * G + 127) / 128;
@@ -195,7 +196,7 @@ pa_status prefill_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   const size_t slots = (size_t)num_tokens * num_heads * ks;
   pl->tok_bytes = align256((size_t)num_tokens * sizeof(int32_t));
   pl->ml_bytes = align256(slots * 2 * sizeof(float));
-  pl->ws_bytes = pl->tok_bytes + pl->ml_bytes + slots * 128 * sizeof(float);
+  pl->ws_bytes = pl->tok_bytes + pl->ml_bytes + slots * (size_t)head_dim * sizeof(float);
   return PA_OK;
 }
 
@@ -433,10 +434,10 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t 
                                   int32_t max_blocks_per_seq, int32_t max_query_len,
                                   int32_t kv_split) {
   if (check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                  0) != PA_OK || head_dim != 128 || max_query_len < 0)
+                  0) != PA_OK || (head_dim != 64 && head_dim != 128) || max_query_len < 0)
     return 0;
   PrefillPlan pl;
-  if (prefill_plan(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+  if (prefill_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                    max_query_len, num_tokens, kv_split, &pl) != PA_OK)
     return 0;
   return pl.ws_bytes;
@@ -458,10 +459,10 @@ static pa_status prefill_call(void* out, const void* query, const void* key_cach
                              max_blocks_per_seq, 0);
   if (st != PA_OK) return st;
   if (max_query_len < 0 || num_tokens < 0) return PA_ERR_BAD_SHAPE;
-  if (dt == DT::F32 || head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (dt == DT::F32 || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
   if ((flags & ~PA_PREFILL_BF16_P) != 0) return PA_ERR_UNSUPPORTED;
   PrefillPlan pl;
-  st = prefill_plan(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+  st = prefill_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                     max_query_len, num_tokens, kv_split, &pl);
   if (st != PA_OK) return st;
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
@@ -512,7 +513,7 @@ static pa_status prefill_call(void* out, const void* query, const void* key_cach
   const bool split_p = !(dt == DT::BF16 && (flags & PA_PREFILL_BF16_P));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = pa::launch_prefill_mfma(dt, kv8, block_size, split_p, p, (int)grid, s);
+  hipError_t e = pa::launch_prefill_mfma(dt, kv8, head_dim, block_size, split_p, p, (int)grid, s);
   if (e != hipSuccess || pl.kv_splits == 1) return launch_status(e);
   // combine the split partials: every query token is a "sequence" whose context is its
   // position + 1, partitioned by the split length

@@ -447,6 +447,10 @@ PREFILL_CONFIGS = {
     # grouped-query heads, ragged chunks, long prefixes
     "prefill_gqa": PrefillSpec("prefill_gqa", 7, 8, 32, 8, 128, "bf16", 16,
                                ("uniform", 0, 3000), ("uniform", 1, 700)),
+    # GPT-OSS-shaped heads (64 query heads on 8 KV heads of 64 dims, the published gpt-oss-20b
+    # attention shape): 512-token chunks on 0..1536 cached tokens
+    "prefill_gptoss_d64": PrefillSpec("prefill_gptoss_d64", 8, 16, 64, 8, 64, "bf16", 16,
+                                      ("uniform", 0, 1536), ("fixed", [512] * 16)),
     # the Llama-7B-shaped chunked prefill over an E4M3 cache
     "prefill_llama7b_fp8": PrefillSpec("prefill_llama7b_fp8", 6, 32, 32, 32, 128, "bf16", 16,
                                        ("uniform", 0, 1536), ("fixed", [512] * 32), kv_dtype="fp8"),

@@ -166,7 +166,8 @@ def test_prefill_fp8_argument_errors(lib):
     assert _prefill_fp8(lib, vs=float("nan")) == 2
     assert _prefill_fp8(lib, out=0) == 1                        # PA_ERR_NULL_PTR
     assert _prefill_fp8(lib, dtype=0) == 3                      # f32 queries: unsupported
-    assert _prefill_fp8(lib, D=64) == 3
+    assert _prefill_fp8(lib, D=256) == 3
+    assert _prefill_fp8(lib, D=64, out=0) == 1
     assert _prefill_fp8(lib, flags=0x2) == 3
     assert _prefill_fp8(lib, flags=0x1, out=0) == 1             # bf16 probabilities accepted
     assert _prefill_fp8(lib, split=512, maxb=64) == 4           # a split needs the workspace
@@ -222,7 +223,9 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, NB=0) == 2
     assert _prefill(lib, scale=float("inf")) == 2
     assert _prefill(lib, dtype=0) == 3               # PA_ERR_UNSUPPORTED: f32
-    assert _prefill(lib, D=64) == 3
+    assert _prefill(lib, D=80) == 3
+    assert _prefill(lib, D=256) == 3
+    assert _prefill(lib, D=64, out=0) == 1          # head dim 64 accepted
     assert _prefill(lib, BS=4) == 3
     assert _prefill(lib, BS=8, out=0) == 1            # 8-token blocks accepted
     assert _prefill(lib, flags=0x2) == 3

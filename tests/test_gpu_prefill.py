@@ -68,8 +68,8 @@ def vmax_of(case: W.PrefillCase) -> float:
     return m
 
 
-def _spec(dtype, bs, Hq, Hkv, prefix, chunk, seed, **kw):
-    return W.PrefillSpec("t", seed, len(prefix), Hq, Hkv, 128, dtype, bs, ("fixed", list(prefix)),
+def _spec(dtype, bs, Hq, Hkv, prefix, chunk, seed, D=128, **kw):
+    return W.PrefillSpec("t", seed, len(prefix), Hq, Hkv, D, dtype, bs, ("fixed", list(prefix)),
                          ("fixed", list(chunk)), **kw)
 
 
@@ -367,3 +367,38 @@ def test_plain_pa_prefill_entry():
     assert st == 0, ops.status_string(st)
     torch.cuda.synchronize()
     assert np.array_equal(bits(W.from_torch(out, "bf16"), "bf16"), bits(ref, "bf16"))
+
+
+# head dim 64 (GPT-OSS-style heads: 8 query heads per KV head); the last case splits the keys
+MATRIX_D64 = [
+    ("bf16", 16, 16, 2, (0, 5, 100, 37), (1, 17, 130, 64), 0),
+    ("f16", 32, 8, 8, (0, 90, 17), (40, 3, 100), 0),
+    ("bf16", 8, 8, 2, (0, 7, 101), (9, 64, 70), 0),
+    ("bf16", 64, 16, 2, (300, 1200), (77, 33), 128),
+]
+
+
+@pytest.mark.parametrize("dtype,bs,Hq,Hkv,prefix,chunk,kv_split", MATRIX_D64)
+def test_prefill_head_dim_64(dtype, bs, Hq, Hkv, prefix, chunk, kv_split):
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec(dtype, bs, Hq, Hkv, prefix, chunk, seed=400 + sum(chunk), D=64))
+    say(f"prefill d64 {dtype} bs{bs} Hq{Hq} Hkv{Hkv} prefix={prefix} chunk={chunk} split={kv_split}")
+    got = Prefill(case, dev).run(kv_split=kv_split)
+    assert_attention_close(got, oracle_prefill(case), dtype, vmax_of(case), "prefill d64")
+
+
+def test_prefill_head_dim_64_poison_and_bf16_p():
+    """Head dim 64: NaN in unused slots and junk table entries change no bit; the single-product
+    mode meets the bound of its one rounding."""
+    dev = need_gpu()
+    spec = _spec("bf16", 16, 16, 2, (0, 64, 300), (100, 64, 40), seed=41, D=64)
+    clean = W.build_prefill_case(spec)
+    say("prefill d64 poison + bf16_p")
+    a = Prefill(clean, dev).run()
+    b = Prefill(W.build_prefill_case(spec, poison=True, table_fill=2**31 - 1), dev).run(fill=0x7FC0)
+    assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
+    ref = oracle_prefill(clean)
+    ref_r = oracle.storage_to_f64(oracle.f64_to_storage(ref, "bf16"), "bf16")
+    g = oracle.storage_to_f64(Prefill(clean, dev).run(bf16_p=True), "bf16")
+    assert np.linalg.norm(g - ref_r) / np.linalg.norm(ref_r) <= 4e-3
+    assert np.max(np.abs(g - ref_r)) <= 1e-2 * vmax_of(clean)

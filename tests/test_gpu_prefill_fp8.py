@@ -23,8 +23,8 @@ K_SCALE = np.float32(W.FP8_DRAW_SCALE)       # pools drawn as N(0,1) / (1/64)
 V_SCALE = np.float32(W.FP8_DRAW_SCALE * 0.5)
 
 
-def _spec(dtype, bs, Hq, Hkv, prefix, chunk, seed):
-    return W.PrefillSpec("fp8p", seed, len(prefix), Hq, Hkv, 128, dtype, bs,
+def _spec(dtype, bs, Hq, Hkv, prefix, chunk, seed, D=128):
+    return W.PrefillSpec("fp8p", seed, len(prefix), Hq, Hkv, D, dtype, bs,
                          ("fixed", list(prefix)), ("fixed", list(chunk)), kv_dtype="fp8")
 
 
@@ -84,11 +84,12 @@ MATRIX = [
 ]
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("dtype,bs,Hq,Hkv,prefix,chunk,kv_split", MATRIX)
-def test_prefill_fp8_matches_oracle(dtype, bs, Hq, Hkv, prefix, chunk, kv_split):
+def test_prefill_fp8_matches_oracle(dtype, bs, Hq, Hkv, prefix, chunk, kv_split, D):
     dev = need_gpu()
-    case = W.build_prefill_case(_spec(dtype, bs, Hq, Hkv, prefix, chunk, seed=300 + sum(chunk)))
-    say(f"prefill_fp8 {dtype} bs{bs} Hq{Hq} Hkv{Hkv} prefix={prefix} chunk={chunk} split={kv_split}")
+    case = W.build_prefill_case(_spec(dtype, bs, Hq, Hkv, prefix, chunk, seed=300 + sum(chunk), D=D))
+    say(f"prefill_fp8 d{D} {dtype} bs{bs} Hq{Hq} Hkv{Hkv} prefix={prefix} chunk={chunk} split={kv_split}")
     got = Run(case, dev)(kv_split=kv_split)
     assert_attention_close(got, _oracle(case), dtype, _vmax(case), "prefill_fp8")
 
