@@ -180,6 +180,15 @@ __device__ __forceinline__ uint4 load_stream(const void* ptr) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Split partials (fp32 normalised outputs of a partition) are written with the non-temporal
+// hint: stored the ordinary way they cost the matrix-core decode ~3% on long GQA contexts
+// (timing-only copies without the stores), written this way ~1-2% (the merge that reads them
+// back right after is not slower).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(float* ptr, float a, float b, float c, float d) {
+  __builtin_nontemporal_store((f32x4_t){a, b, c, d}, reinterpret_cast<f32x4_t*>(ptr));
+}
+
 // K/V tile load: streaming by default; an ordinary (cache-allocating) load when the caller
 // says blocks are shared by several sequences of the call, so later readers hit in L2.
 template <bool STREAM>

@@ -543,8 +543,8 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     } else {
       const size_t slot = ((size_t)s * p.num_heads + h0 + h) * p.max_parts + p0 + k;
       float* po = p.ws_o + slot * D + cc * 8;
-      *reinterpret_cast<float4*>(po) = make_float4(O[0], O[1], O[2], O[3]);
-      *reinterpret_cast<float4*>(po + 4) = make_float4(O[4], O[5], O[6], O[7]);
+      store_stream(po, O[0], O[1], O[2], O[3]);
+      store_stream(po + 4, O[4], O[5], O[6], O[7]);
       if (cc == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(Mx, L);
     }
   }

@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       float* po = p.ws_o + slot * D + cc * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(po + e) = make_float4(O[e], O[e + 1], O[e + 2], O[e + 3]);
+        store_stream(po + e, O[e], O[e + 1], O[e + 2], O[e + 3]);
       if (cc == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(M, L);
     }
   }
