@@ -367,9 +367,9 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key
  * (pa_decode_workspace_bytes with the same sizes), flags and errors as pa_decode_ex.
  * pa_decode_fp8_partitions is its first launch (pa_decode_merge, with the same dtype, is the
  * second).  Supported: head_dim 64, 80, 128 or 256, block_size 8, 16, 32, 64 or 128.  When
- * head_dim is 128 and num_heads / num_kv_heads is a multiple of 4 (and partition_size one of 16)
- * the grouped heads run on the matrix cores, the codes converted exactly to dtype in registers;
- * otherwise on the vector ALUs.
+ * head_dim is 64, 128 or 256 and num_heads / num_kv_heads is a multiple of 4 (and partition_size
+ * one of 16) the grouped heads run on the matrix cores, the codes converted exactly to dtype in
+ * registers; otherwise on the vector ALUs.
  */
 pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
                         const void* value_cache, const int32_t* block_tables,

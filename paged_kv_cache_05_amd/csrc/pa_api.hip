@@ -625,8 +625,7 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   // Grouped heads (a multiple of 4) run on the matrix cores, which read each K/V byte once per
   // KV head; otherwise the vector-ALU kernel, at most 2 heads per workgroup (16 fp32 outputs
   // per lane per head).
-  // (the 8-bit matrix-core kernel is built for head dim 128)
-  const bool mfma = mfma_eligible(dt, head_dim, G, pl.partition) && head_dim == 128;
+  const bool mfma = mfma_eligible(dt, head_dim, G, pl.partition);
   const int gt = mfma ? heads_per_wg(true, G, head_dim) : std::min(heads_per_wg(false, G, head_dim), 2);
 
   pa::DecodeParams p;

@@ -296,6 +296,9 @@ hipError_t launch_decode_mfma_d256(DT dt, int block_size, int heads_per_wg, bool
                                    const DecodeParams& p, int grid, hipStream_t st);
 hipError_t launch_decode_mfma_fp8(DT dt, int head_dim, int block_size, int heads_per_wg,
                                   bool stream_kv, const DecodeParams& p, int grid, hipStream_t st);
+hipError_t launch_decode_mfma_fp8_dims(DT dt, int head_dim, int block_size, int heads_per_wg,
+                                       bool stream_kv, const DecodeParams& p, int grid,
+                                       hipStream_t st);
 hipError_t launch_prefill_mfma(DT dt, bool kv8, int head_dim, int block_size, bool split_p,
                                const PrefillParams& p, int grid, hipStream_t st);
 hipError_t launch_prefill_mfma_d64(DT dt, bool kv8, int block_size, bool split_p,

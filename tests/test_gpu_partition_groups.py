@@ -46,9 +46,7 @@ SHAPES = [
 ]
 
 
-# the 8-bit matrix-core kernel is built for head dim 128 only
-CASES = [(*shape, kv) for shape in SHAPES for kv in ("bf16", "f16", "fp8")
-         if kv != "fp8" or shape[5] == 128]
+CASES = [(*shape, kv) for shape in SHAPES for kv in ("bf16", "f16", "fp8")]
 
 
 @pytest.mark.parametrize("Hq,Hkv,S,width,P,D,kv", CASES)
