@@ -110,3 +110,52 @@ def test_prefill_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(W.from_torch(out, "bf16"), "bf16"), bits(eager, "bf16")), r
+
+
+def test_prefill_fp8_split_graph_replays():
+    """pa_prefill_fp8 with its keys split (two launches: the partials, then the merge) over
+    E4M3 pools, captured and replayed with unrelated eager work between replays: every replay
+    gives the eager bits."""
+    import torch
+    dev = need_gpu()
+    spec = W.PrefillSpec("g8", 32, 3, 8, 2, 128, "bf16", 16, ("fixed", [0, 300, 700]),
+                         ("fixed", [70, 40, 129]), kv_dtype="fp8")
+    case = W.build_prefill_case(spec)
+    say("graph replay: prefill_fp8 with key splits")
+    q = W.to_torch(case.query, "bf16", dev)
+    kc = W.to_torch(case.pool.key_cache, "fp8", dev)
+    vc = W.to_torch(case.pool.value_cache, "fp8", dev)
+    bt = torch.from_numpy(np.ascontiguousarray(case.pool.block_tables, np.int32)).to(dev)
+    qsl = torch.from_numpy(np.ascontiguousarray(case.query_start_loc, np.int32)).to(dev)
+    cl = torch.from_numpy(np.ascontiguousarray(case.context_lens, np.int32)).to(dev)
+    out = torch.empty_like(q)
+    need = ops.prefill_workspace_bytes(3, q.shape[0], 8, 2, 128, 16, bt.shape[1],
+                                       case.max_query_len, 128)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ks, vs = W.FP8_DRAW_SCALE, W.FP8_DRAW_SCALE * 0.5
+
+    def run():
+        ops.prefill_fp8(out, q, kc, vc, bt, qsl, cl, float(case.scale), case.max_query_len,
+                        ks, vs, kv_split=128, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    eager = W.from_torch(out, "bf16").copy()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    junk = torch.empty(1 << 20, dtype=torch.float32, device=dev)
+    for r in range(3):
+        out.view(torch.int16).fill_(-1)
+        ws.fill_(0xFF)
+        junk.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(W.from_torch(out, "bf16"), "bf16"), bits(eager, "bf16")), r
