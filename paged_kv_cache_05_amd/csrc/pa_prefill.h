@@ -101,9 +101,21 @@ constexpr float kLazy = 8.0f;    // running-max slack (log2 units): probabilitie
 
 __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
+// With ON, the value as an opaque register: the compiler must take it as changed here, so the
+// addresses derived from it are recomputed where they are used (one XOR each) instead of being
+// hoisted out of the loop into a register apiece.  At head dim 64 (three waves per SIMD, 168
+// registers) the hoisted addresses made the 16-bit instances spill 11-12 values; recomputed,
+// they fit in 154-162 and the GPT-OSS-shaped prefill ran 6-11% faster.  At head dim 128 (two
+// waves per SIMD) hoisting costs nothing and the 8-bit instances ran ~1% slower without it.
+template <bool ON>
+__device__ __forceinline__ int opaque(int v) {
+  if constexpr (ON) asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Two workgroups per CU (two waves per SIMD, up to 256 registers) at D = 128.  At D = 64 the
-// kernel is asked for three: the 8-bit instances then fit 162-168 registers, the 16-bit ones
-// spill 11-12 values, and the GPT-OSS-shaped prefill still runs 6-7% faster than at two.
+// kernel is asked for three (168 registers): with the LDS addresses recomputed (opaque<>) every
+// instance fits in 142-162 with no spills.
 template <DT dt, int D, int BS, bool SPLIT_P, bool K8>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(const PrefillParams p) {
   using M = Mma<dt>;
@@ -273,6 +285,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
   // so the 8 tokens one MFMA lane needs (4g+i of 16-token blocks 2h and 2h+1) are contiguous.
   const int v_chunk = 4 * (tg >> 3) + (tg & 3);
   const int v_half = (tg >> 2) & 1;
+  // Swizzles split into a lane part and a compile-time part: the K chunk of the thread's token
+  // 4tg + i is sk ^ i, the V^T chunk of its dim 8dc + e is sv ^ e; the score operand of lane
+  // (lr, lg) at depth step c of token block j is klane ^ 4c (^ 2j mod 8 with 8 chunks a row);
+  // the V^T operand of half h at dim block b is vlane[h] ^ (2b mod 8).
+  const int sk = dc ^ kswz(4 * tg);
+  const int sv = v_chunk ^ (dc & 7);
+  const int klane = lg ^ (CH == 16 ? lr : ((lr & 7) ^ (lr >> 3)));
+  const int vlane[2] = {lg ^ (lr & 7) ^ (lr >> 3), (4 + lg) ^ (lr & 7) ^ (lr >> 3)};
   // a loaded row piece as 8 values of dt (16 bytes): as loaded, or 8 E4M3 codes widened
   auto widen = [](const Raw& r) -> uint4 {
     if constexpr (K8) {
@@ -282,6 +302,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
     }
   };
   auto stash = [&](int buf) {
+    const int skx = opaque<D == 64>(sk), svx = opaque<D == 64>(sv);
     uint4 kw[4], vw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -291,12 +312,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * tg + i;
-      s_k[buf][t * CH + (dc ^ kswz(t))] = kw[i];
+      s_k[buf][t * CH + (skx ^ i)] = kw[i];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = 8 * dc + e;
-      char* dst = reinterpret_cast<char*>(&s_v[buf][d * 8 + (v_chunk ^ vswz(d))]) + 8 * v_half;
+      char* dst = reinterpret_cast<char*>(&s_v[buf][d * 8 + (svx ^ e)]) + 8 * v_half;
       *reinterpret_cast<uint2*>(dst) = tile_column(vw, e);
     }
   };
@@ -333,13 +354,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
   // MFMA / VALU interleave with scheduling-group barriers measured much slower.
   using St = f32x4[2][2];   // [16-token block][row block]
   auto scores = [&](St& st, int buf, int h) {
+    const int kl = opaque<D == 64>(klane);
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       const int j = 2 * h + jb;
       st[jb][0] = st[jb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const uint4 a = s_k[buf][(16 * j + lr) * CH + ((4 * c + lg) ^ kswz(16 * j + lr))];
+        const uint4 a = s_k[buf][(16 * j + lr) * CH + (kl ^ (4 * c) ^ (CH == 16 ? 0 : (2 * j) & 7))];
         st[jb][0] = M::mma(a, qb[0][c], st[jb][0]);
         st[jb][1] = M::mma(a, qb[1][c], st[jb][1]);
       }
@@ -407,6 +429,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
     }
   };
   auto accumulate = [&](const uint4 (&ph)[2], const uint4 (&pl)[2], int buf, int h) {
+    const int vl = opaque<D == 64>(vlane[h]);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       l_acc[c2] = M::mma(ones, ph[c2], l_acc[c2]);
@@ -415,7 +438,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
 #pragma unroll
     for (int dt2 = 0; dt2 < NDB; ++dt2) {
       const int d = 16 * dt2 + lr;
-      const uint4 a = s_v[buf][d * 8 + ((4 * h + lg) ^ vswz(d))];
+      const uint4 a = s_v[buf][d * 8 + (vl ^ ((2 * dt2) & 7))];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) o[dt2][c2] = M::mma(a, ph[c2], o[dt2][c2]);
       if constexpr (SPLIT_P) {
