@@ -106,7 +106,7 @@ __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
 // hoisted out of the loop into a register apiece.  At head dim 64 (three waves per SIMD, 168
 // registers) the hoisted addresses made the 16-bit instances spill 11-12 values; recomputed,
 // they fit in 154-162 and the GPT-OSS-shaped prefill ran 6-11% faster.  At head dim 128 (two
-// waves per SIMD) hoisting costs nothing and the 8-bit instances ran ~1% slower without it.
+// waves per SIMD) hoisting costs nothing, and recomputing made the 8-bit instances ~1% slower.
 template <bool ON>
 __device__ __forceinline__ int opaque(int v) {
   if constexpr (ON) asm volatile("" : "+v"(v));
