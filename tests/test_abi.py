@@ -196,7 +196,7 @@ def test_prefill_split_plan_and_errors(lib):
     """Key splits: the workspace query, the library's choice (split only small grids), an
     explicit split length, and the argument errors of pa_prefill_ex."""
     ws = lib.pa_prefill_workspace_bytes
-    # 4 seqs x 2 KV heads x 4 row tiles = 32 workgroups over 1024-token tables: split
+    # 4 seqs x 2 KV heads x 2 row tiles = 16 workgroups over 1024-token tables: split
     auto = ws(4, 100, 8, 2, 128, 16, 64, 64, 0)
     assert auto > 0
     # 256 x 32 heads x 4 row tiles: the grid fills the GPU, no split
