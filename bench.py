@@ -149,6 +149,8 @@ class Step:
             ev[1].record()
         ops.decode_merge(self.out, self.cl, self.case.spec.num_kv_heads, self.case.spec.block_size,
                          self.case.max_blocks_per_seq, self.ws, partition_size=self.P)
+        if ev is not None and len(ev) > 2:
+            ev[2].record()
 
 
 def time_steps(step, steps, warmup):
@@ -156,8 +158,8 @@ def time_steps(step, steps, warmup):
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    # per step: before the decode kernel, between it and the merge, after the merge
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -169,8 +171,9 @@ def time_steps(step, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    kern = [a.elapsed_time(b) for a, b in evs]
+    kern = [a.elapsed_time(b) for a, b, _ in evs]
     step.last_kernel_ms = kern
+    step.last_merge_ms = [b.elapsed_time(c) for _, b, c in evs]
     return total_ms / steps, float(np.mean(kern)), float(np.min(kern)), wall
 
 
@@ -686,6 +689,9 @@ def main(argv=None):
             "median_launch_ms": round(float(np.median(step.last_kernel_ms)), 4),
             "algorithmic_bytes_per_launch": dbytes,
         },
+        # the split-KV merge launch that follows the decode kernel in each step (it exits at
+        # once for sequences held in one partition)
+        "merge_kernel_ms": round(float(np.mean(step.last_merge_ms)), 4),
     }
     if case.snaps is not None:
         cpu_legs[name] = cpu_baseline_leg(case, case.snaps, args.cpu_seconds, CPU_BASELINE_LEGS[name])
@@ -704,6 +710,7 @@ def main(argv=None):
                          "seq_heads_per_s": round(c2.spec.num_seqs * c2.spec.num_heads / (ms2 * 1e-3), 1),
                          "kernel": chosen_kernel(c2, args.kernel)}
         detail[extra]["decode_kernel_median_ms"] = round(float(np.median(step.last_kernel_ms)), 4)
+        detail[extra]["merge_kernel_ms"] = round(float(np.mean(step.last_merge_ms)), 4)
         ub = decode_unique_kv_bytes(c2)
         if c2.spec.shared_prefix:
             detail[extra]["unique_kv_bytes"] = ub
