@@ -117,6 +117,18 @@ def test_prefill_bf16_probabilities_flag():
     assert_attention_close(run.run(), ref, "bf16", vmax_of(case), "prefill split")
 
 
+def test_prefill_peaked_rows():
+    """Rows whose attention falls on a few keys have outputs close to max|V|: queries scaled
+    by 40 (a near one-hot softmax) over cached prefixes and whole prompts, against the oracle."""
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec("bf16", 16, 8, 2, (0, 200, 0, 900), (150, 70, 33, 128),
+                                      seed=62))
+    case.query = oracle.f64_to_storage(oracle.storage_to_f64(case.query, "bf16") * 40.0, "bf16")
+    say("prefill peaked rows")
+    got = Prefill(case, dev).run()
+    assert_attention_close(got, oracle_prefill(case), "bf16", vmax_of(case), "peaked rows")
+
+
 def test_prefill_single_token_chunks_equal_decode():
     """One-token chunks are decodes: the prefill kernel agrees bit-for-bit with itself across
     calls and within the attention bar of the decode oracle."""
