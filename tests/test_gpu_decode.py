@@ -139,7 +139,7 @@ def test_mfma_head_dims_64_256(dtype, D, BS, heads):
         assert np.array_equal(bits(ub.decode("mfma", P), dtype), bits(got, dtype))
 
 
-_GROUPINGS = [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1)]
+_GROUPINGS = [(4, 4), (6, 3), (8, 8), (12, 3), (16, 2), (32, 2), (16, 1), (32, 1), (12, 1), (24, 1)]
 
 
 @pytest.mark.parametrize("heads,kernel", [(h, k) for h in _GROUPINGS for k in ("valu", "mfma")

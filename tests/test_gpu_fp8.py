@@ -65,6 +65,8 @@ MATRIX = [
     ("bf16", 8, 8, 2, (1, 7, 8, 9, 300), 16),         # 8-token blocks, one-chunk partitions
     ("f16", 16, 16, 4, (1, 15, 17, 640, 333), 64),    # G = 4 with f16 queries (matrix cores)
     ("bf16", 32, 16, 2, (5, 100, 1100), 0),           # G = 8: 8 heads per workgroup
+    ("bf16", 16, 12, 1, (1, 16, 300, 777), 128),      # G = 12: three 4-head workgroups per KV head
+    ("bf16", 16, 32, 1, (17, 513, 1500), 0),          # G = 32: two 16-head workgroups
 ]
 
 
