@@ -23,7 +23,8 @@
 //     exactly the four scores the lane already holds, so P never moves between lanes.  The B
 //     operand needs four tokens of one column per lane: lane l loads dims (D/16)(l%16) .. of
 //     tokens 4(l/16) .. +4 (the 16 lanes of a token group cover whole rows) and transposes the
-//     4 x D/16 16-bit tile in registers with v_perm_b32.
+//     4 x D/16 16-bit tile in registers with v_perm_b32 (8-bit rows: the codes are gathered by
+//     byte permutes first, then converted two at a time straight into operand order).
 //   P is split into a 16-bit high part and a 16-bit remainder (two MFMAs per column group), so
 //   the probabilities keep about 16 significant bits instead of the 8 of one bfloat16.
 // Softmax state: a running reference point per head, shared by the four lanes holding that head
@@ -107,6 +108,22 @@ __device__ __forceinline__ uint2 fp8x4_to_16bit(uint32_t w) {
     return make_uint2(
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+  }
+}
+
+// The two 16-bit values of dim e (byte e % 4 of word e / 4) of four tokens' E4M3 rows, in
+// token order: x01 / x23 hold the bytes k, k+1 (k = e & 2) of tokens 0, 1 / 2, 3 interleaved
+// (one v_perm_b32 each, shared by dims k and k+1), and one scaled packed conversion of a half
+// word turns two codes into two 16-bit values.  Gathering the codes before converting takes
+// half the permutes of transposing the converted 16-bit values.
+template <class M>
+__device__ __forceinline__ uint32_t fp8x2_to_16bit(uint32_t w, bool hi) {
+  if constexpr (std::is_same_v<M, Mfma<DT::BF16>>) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  } else {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
   }
 }
 
@@ -417,26 +434,36 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     const uint2 phi = make_uint2(h01, h23);
     const uint2 plo = make_uint2(M::pack2(pv[0] - M::lo(h01), pv[1] - M::hi(h01)),
                                  M::pack2(pv[2] - M::lo(h23), pv[3] - M::hi(h23)));
-    uint32_t vb[4][DPL / 2];   // this lane's 4 V rows (dims DPL lr ..) as 16-bit values
+    if constexpr (K8) {
+      // word w of row j holds the codes of dims DPL lr + 4w .. +3 of token 4kg + j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (K8) {
+      for (int w = 0; w < VW; ++w) {
 #pragma unroll
-        for (int w = 0; w < VW; ++w) {
-          const uint2 a = fp8x4_to_16bit<M>(c.v[j][w]);
-          vb[j][2 * w] = a.x;
-          vb[j][2 * w + 1] = a.y;
+        for (int k = 0; k < 4; k += 2) {
+          const uint32_t sel = k == 0 ? 0x05010400u : 0x07030602u;
+          const uint32_t x01 = __builtin_amdgcn_perm(c.v[1][w], c.v[0][w], sel);
+          const uint32_t x23 = __builtin_amdgcn_perm(c.v[3][w], c.v[2][w], sel);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int e = 4 * w + k + b;
+            const uint2 bv = make_uint2(fp8x2_to_16bit<M>(x01, b), fp8x2_to_16bit<M>(x23, b));
+            acc[e] = M::mma16(phi, bv, acc[e]);
+            acc[e] = M::mma16(plo, bv, acc[e]);
+          }
         }
-      } else {
+      }
+    } else {
+      uint32_t vb[4][DPL / 2];   // this lane's 4 V rows (dims DPL lr ..) as 16-bit values
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int w = 0; w < VW; ++w) vb[j][w] = c.v[j][w];
-      }
-    }
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const uint2 bv = tile_column_words<DPL / 2>(vb, e);
-      acc[e] = M::mma16(phi, bv, acc[e]);
-      acc[e] = M::mma16(plo, bv, acc[e]);
+      for (int e = 0; e < DPL; ++e) {
+        const uint2 bv = tile_column_words<DPL / 2>(vb, e);
+        acc[e] = M::mma16(phi, bv, acc[e]);
+        acc[e] = M::mma16(plo, bv, acc[e]);
+      }
     }
     // a countdown, not a division by the runtime Q: full partitions hold Q chunks per wave
     if (np_wg > 1 && --left == 0) {

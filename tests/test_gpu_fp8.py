@@ -335,3 +335,26 @@ def test_decode_fp8_every_code_one_token(dtype, Hq, Hkv):
     for s in range(S):
         seen.update(vc[int(case.block_tables[s][0]), :, 0, :].ravel().tolist())
     assert seen == set(codes.tolist())
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883, -2.0])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_decode_fp8_zero_and_negative_scale(scale, D):
+    """Grouped heads over an 8-bit cache (the matrix-core kernel, which compares raw scores and
+    carries a negative scale in the query signs): scale 0 gives the mean of V, a negative scale
+    reverses the ordering of the scores -- against the oracle, single pass and split."""
+    import torch
+    dev = need_gpu()
+    case = W.build_case(_spec("bf16", 16, 16, 4, (1, 17, 300, 1000), seed=260 + D, D=D))
+    case.scale = np.float32(scale)
+    q, kc, vc, bt, cl = _upload(case, dev)
+    ref = _oracle(case)
+    vmax = _vmax(case, oracle.dequantize_fp8(case.value_cache, V_SCALE))
+    for P in (0, 64):
+        say(f"decode_fp8 D={D} scale={scale} P={P}")
+        out = torch.empty_like(q)
+        ops.decode_fp8(out, q, kc, vc, bt, cl, float(case.scale), float(K_SCALE), float(V_SCALE),
+                       partition_size=P)
+        torch.cuda.synchronize()
+        assert_attention_close(W.from_torch(out, "bf16"), ref, "bf16", vmax,
+                               f"fp8 scale {scale} D={D} P={P}")
