@@ -160,16 +160,50 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b) of two permlane-swap results as one v_max_f32.  fmaxf would first pass each
+// operand through a canonicalising v_max (x, x), since the compiler cannot tell that a
+// permlane output is no signalling NaN; these values are scores, -inf or NaNs that arithmetic
+// produced, for which v_max_f32 alone gives the same result.  Only for operands written by a
+// permlane swap: inline asm gets no hazard wait states from the compiler, and a VALU read right
+// after a permlane swap needs none, while one right after an MFMA would.
+__device__ __forceinline__ float max_of_swapped(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Max over the four lanes l, l^16, l^32, l^48 (one query row of an MFMA output).  Each
 // permlane swap leaves, in every lane, its own value and its partner's (lane ^ 32, then
 // lane ^ 16) in the two results, whichever result holds which.
 __device__ __forceinline__ float row_max4(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_of_swapped(a[0], a[1]);
   const uint32_t w = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_of_swapped(b[0], b[1]);
+}
+
+// max of four values that vector-ALU instructions wrote (products, selects; never MFMA results,
+// for the reason given at max_of_swapped), as v_max3_f32 + v_max_f32
+__device__ __forceinline__ float max4_valu(float a, float b, float c, float d) {
+  float r, t;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(t) : "v"(a), "v"(b), "v"(c));
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(t), "v"(d));
+  return r;
+}
+
+// max(m, row_max4(x)), the last step one v_max3_f32 (m: a value the vector ALUs wrote, such
+// as a running max, never an MFMA result)
+__device__ __forceinline__ float row_max4_with(float m, float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = max_of_swapped(a[0], a[1]);
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(b[0]), "v"(b[1]));
+  return r;
 }
 
 // Streaming 16-byte load: K/V tiles are read exactly once per call, so they are fetched with

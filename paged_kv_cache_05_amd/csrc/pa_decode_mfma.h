@@ -402,12 +402,11 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     }
     // chunk max per head over the four token groups (lanes l, l^16, l^32, l^48), with
     // permlane swaps on the vector ALUs rather than LDS round trips
-    const float bm = row_max4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const float mn = row_max4_with(m_run, max4_valu(sv[0], sv[1], sv[2], sv[3]));
     // Lazy reference point: it moves only when a head's max exceeds it by more than kLazy
     // (always on the first live chunk, from -inf), so probabilities stay below 2^kLazy and the
     // rescale -- four cross-lane shuffles and 4 D/16 multiplies -- runs on few chunks instead of on
     // every chunk that sets a new max.  Any reference point gives the same o / l.
-    const float mn = fmaxf(m_run, bm);
     const bool grow = mn > m_run + kLazy;
     if (__any(grow)) {
       const float alpha = grow ? fast_exp2(m_run - mn) : 1.0f;
