@@ -296,7 +296,8 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
  * Rows of a sequence with L_s > n, or n > max_blocks_per_seq * block_size, are written as
  * zeros; rows past max_query_len of a longer chunk are not written.  Only the first
  * ceil(n / block_size) table entries and the first n slots are read.
- * Supported: dtype f16 or bf16, head_dim 64 or 128, block_size 8, 16, 32, 64 or 128.  Arithmetic: 16-bit
+ * Supported: dtype f16 or bf16, head_dim 64, 80 or 128 (80: the 128-dim products with dims
+ * 80 .. 127 held as zeros, never loaded or stored), block_size 8, 16, 32, 64 or 128.  Arithmetic: 16-bit
  * operands on the matrix cores with fp32 accumulation; the softmax probabilities keep about
  * 16 significant bits for bf16 (two products) and 11 for f16, unless flags has
  * PA_PREFILL_BF16_P, which rounds bf16 probabilities to bfloat16 once (one product, faster,

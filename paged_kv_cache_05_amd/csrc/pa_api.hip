@@ -429,12 +429,15 @@ pa_status pa_swap_blocks(const void* src_key_cache, const void* src_value_cache,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Head dims of the prefill kernel: 64 and 128, and 80 (the 128-dim products on zero-padded rows).
+static bool prefill_head_dim(int32_t d) { return d == 64 || d == 80 || d == 128; }
+
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                   int32_t max_blocks_per_seq, int32_t max_query_len,
                                   int32_t kv_split) {
   if (check_shape(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                  0) != PA_OK || (head_dim != 64 && head_dim != 128) || max_query_len < 0)
+                  0) != PA_OK || !prefill_head_dim(head_dim) || max_query_len < 0)
     return 0;
   PrefillPlan pl;
   if (prefill_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
@@ -459,7 +462,7 @@ static pa_status prefill_call(void* out, const void* query, const void* key_cach
                              max_blocks_per_seq, 0);
   if (st != PA_OK) return st;
   if (max_query_len < 0 || num_tokens < 0) return PA_ERR_BAD_SHAPE;
-  if (dt == DT::F32 || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (dt == DT::F32 || !prefill_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   if ((flags & ~PA_PREFILL_BF16_P) != 0) return PA_ERR_UNSUPPORTED;
   PrefillPlan pl;
   st = prefill_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,

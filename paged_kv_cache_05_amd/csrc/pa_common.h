@@ -337,6 +337,8 @@ hipError_t launch_prefill_mfma(DT dt, bool kv8, int head_dim, int block_size, bo
                                const PrefillParams& p, int grid, hipStream_t st);
 hipError_t launch_prefill_mfma_d64(DT dt, bool kv8, int block_size, bool split_p,
                                    const PrefillParams& p, int grid, hipStream_t st);
+hipError_t launch_prefill_mfma_d80(DT dt, bool kv8, int block_size, bool split_p,
+                                   const PrefillParams& p, int grid, hipStream_t st);
 hipError_t launch_merge(DT dt, int head_dim, const MergeParams& p, hipStream_t st);
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int64_t* slots, int num_tokens, int row_vecs,

@@ -10,7 +10,9 @@
 // block table exactly as decode reads them.
 //
 // Head dims 64 and 128 (D below; the figures quote D = 128, the GPT-OSS-shaped D = 64 halves
-// the depth steps and output blocks).
+// the depth steps and output blocks), and 80 (DP, the head dim of the queries, outputs and
+// pools, below D): such rows run through the 128-dim products with dims DP .. 127 zero in
+// registers and LDS -- they add nothing to a score and give output dims that are not stored.
 //
 // Work decomposition.  A workgroup (4 waves) owns 128 query rows of one (sequence, KV head):
 // row r is chunk token r / G with query head kvh*G + r % G, so the G heads sharing a KV head
@@ -116,11 +118,13 @@ __device__ __forceinline__ int opaque(int v) {
 // Two workgroups per CU (two waves per SIMD, up to 256 registers) at D = 128.  At D = 64 the
 // kernel is asked for three (168 registers): with the LDS addresses recomputed (opaque<>) every
 // instance fits in 142-162 with no spills.
-template <DT dt, int D, int BS, bool SPLIT_P, bool K8>
+template <DT dt, int D, int BS, bool SPLIT_P, bool K8, int DP = D>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(const PrefillParams p) {
   using M = Mma<dt>;
   static_assert(D == 64 || D == 128, "head dims 64 and 128");
-  constexpr int kD = D;                     // head dim
+  static_assert(DP <= D && DP % 16 == 0, "stored head dim: whole 16-dim output blocks");
+  constexpr int kD = D;                     // head dim of the products
+  constexpr int CHP = DP / 8;               // 16-byte chunks of a stored 16-bit row
   constexpr int kRow = kD * 2;              // bytes of a 16-bit token row
   constexpr int KC = kD / 32;               // 32-dim depth steps of the score product
   constexpr int NDB = kD / 16;              // 16-dim blocks of the output
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
   // K8: E4M3 pools (128-byte token rows); the codes are widened to dt when a tile is stored in
   // LDS, so the products below are the 16-bit ones.  The key scale is folded into scale_log2 by
   // the host, the value scale into the final normalisation.
-  constexpr int CROW = K8 ? kD : kRow;      // bytes of one cached token row
+  constexpr int CROW = K8 ? DP : 2 * DP;    // bytes of one cached token row
   constexpr int CPIECE = K8 ? 8 : 16;       // bytes of a row one loader thread moves
   using Raw = std::conditional_t<K8, uint2, uint4>;
   static_assert(BS % 8 == 0, "a thread's 4 tokens must sit in one block");
@@ -183,15 +187,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
   // element offset of row r's query / output vector
   auto row_off = [&](int r) -> size_t {
     const int t = r / G;
-    return ((size_t)(q0 + t) * p.num_heads + kvh * G + (r - t * G)) * kD;
+    return ((size_t)(q0 + t) * p.num_heads + kvh * G + (r - t * G)) * DP;
   };
 
   if (!fits) {  // the chunk does not fit its context: zeros (from the first key split)
     if (ks != 0) return;
-    for (int idx = tid; idx < kRowsWG * CH; idx += 256) {
-      const int r = row0 + idx / CH;
+    for (int idx = tid; idx < kRowsWG * CHP; idx += 256) {
+      const int r = row0 + idx / CHP;
       if (r < rows)
-        *reinterpret_cast<uint4*>((char*)p.out + row_off(r) * 2 + (idx % CH) * 16) =
+        *reinterpret_cast<uint4*>((char*)p.out + row_off(r) * 2 + (idx % CHP) * 16) =
             make_uint4(0, 0, 0, 0);
     }
     return;
@@ -221,8 +225,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
     const char* qp = (const char*)p.q + row_off(rc) * 2;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      qb[c2][c] = r < rows ? *reinterpret_cast<const uint4*>(qp + (32 * c + 8 * lg) * 2)
-                           : make_uint4(0, 0, 0, 0);
+      qb[c2][c] = r < rows && 32 * c + 8 * lg < DP
+                      ? *reinterpret_cast<const uint4*>(qp + (32 * c + 8 * lg) * 2)
+                      : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       qb[c2][c].x ^= p.q_sign;
@@ -243,6 +248,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
   const int tg = CH == 16 ? (((p16 >> 1) & 3) | ((l16 >> 3) << 2) | ((p16 >> 3) << 3))
                           : (((p16 >> 1) & 3) | ((l16 >> 3) << 2) | ((p16 & 1) << 3));
   const bool loader = CH == 16 || tid < 128;   // wave-uniform
+  // dims 8dc .. 8dc+7 are stored (below DP); the others are zero in LDS
+  const bool dlive = DP == D || 8 * dc < DP;
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int nb_live = (n + BS - 1) / BS;
   const size_t head_off = (size_t)kvh * BS * CROW;
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
                        head_off + (size_t)(t0 % BS) * CROW + dc * CPIECE;
     const char* kp = (const char*)p.kc + off;
     const char* vp = (const char*)p.vc + off;
-    if (t0 + 3 < n) {   // the usual case: four live rows, unconditional loads
+    if (dlive && t0 + 3 < n) {   // the usual case: four live rows, unconditional loads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         kr[i] = *reinterpret_cast<const Raw*>(kp + i * CROW);
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool live = t0 + i < n;
+        const bool live = dlive && t0 + i < n;   // padded dims are never loaded
         Raw zk, zv;
         if constexpr (K8) {
           zk = zv = make_uint2(0, 0);
@@ -491,17 +498,17 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
     if (r < rows && np == 1 && ks == 0) {
       char* op = (char*)p.out + row_off(r) * 2;
 #pragma unroll
-      for (int dt2 = 0; dt2 < NDB; ++dt2) {
+      for (int dt2 = 0; dt2 < DP / 16; ++dt2) {   // stored dims only
         const f32x4 v = o[dt2][c2];
         const uint2 w2 = make_uint2(M::bits(v[0] * inv) | (M::bits(v[1] * inv) << 16),
                                     M::bits(v[2] * inv) | (M::bits(v[3] * inv) << 16));
         *reinterpret_cast<uint2*>(op + (16 * dt2 + 4 * lg) * 2) = w2;
       }
     } else if (r < rows && np > 1 && ks < np && q0 + r / G < p.num_tokens) {
-      const size_t slot = (row_off(r) / kD) * KS + ks;
-      float* po = p.ws_o + slot * kD;
+      const size_t slot = (row_off(r) / DP) * KS + ks;
+      float* po = p.ws_o + slot * DP;
 #pragma unroll
-      for (int dt2 = 0; dt2 < NDB; ++dt2) {
+      for (int dt2 = 0; dt2 < DP / 16; ++dt2) {
         const f32x4 v = o[dt2][c2];
         *reinterpret_cast<float4*>(po + 16 * dt2 + 4 * lg) =
             make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
@@ -511,14 +518,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void prefill_mfma_kernel(cons
   }
 }
 
-template <DT dt, int D, int BS, bool SPLIT, bool K8>
+template <DT dt, int D, int BS, bool SPLIT, bool K8, int DP>
 hipError_t go(const PrefillParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<dt, D, BS, SPLIT, K8>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<dt, D, BS, SPLIT, K8, DP>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-// every instance of head dim D: query type, probability split, cache element, block size
-template <int D>
+// every instance of head dim D (stored head dim DP): query type, probability split, cache
+// element, block size
+template <int D, int DP = D>
 hipError_t launch_prefill_d(DT dt, bool kv8, int block_size, bool split_p,
                             const PrefillParams& p, int grid, hipStream_t st) {
   auto by_bs = [&](auto dt_tag, auto split_tag, auto k8_tag) -> hipError_t {
@@ -526,11 +534,11 @@ hipError_t launch_prefill_d(DT dt, bool kv8, int block_size, bool split_p,
     constexpr bool SP = decltype(split_tag)::value;
     constexpr bool K8 = decltype(k8_tag)::value;
     switch (block_size) {
-      case 8: return go<T, D, 8, SP, K8>(p, grid, st);
-      case 16: return go<T, D, 16, SP, K8>(p, grid, st);
-      case 32: return go<T, D, 32, SP, K8>(p, grid, st);
-      case 64: return go<T, D, 64, SP, K8>(p, grid, st);
-      case 128: return go<T, D, 128, SP, K8>(p, grid, st);
+      case 8: return go<T, D, 8, SP, K8, DP>(p, grid, st);
+      case 16: return go<T, D, 16, SP, K8, DP>(p, grid, st);
+      case 32: return go<T, D, 32, SP, K8, DP>(p, grid, st);
+      case 64: return go<T, D, 64, SP, K8, DP>(p, grid, st);
+      case 128: return go<T, D, 128, SP, K8, DP>(p, grid, st);
     }
     return hipErrorInvalidValue;
   };

@@ -205,6 +205,9 @@ def test_prefill_split_plan_and_errors(lib):
     two = ws(4, 100, 8, 2, 128, 16, 64, 64, 512)                 # two splits: 100 x 8 x 2 slots
     # token lengths (400 B -> 512), (max, denominator) pairs, fp32 partial outputs
     assert two == 512 + 1600 * 2 * 4 + 1600 * 128 * 4
+    # head dim 80: the partials are 80 floats a row; other head dims get no workspace
+    assert ws(4, 100, 8, 2, 80, 16, 64, 64, 512) == 512 + 1600 * 2 * 4 + 1600 * 80 * 4
+    assert ws(4, 100, 8, 2, 256, 16, 64, 64, 512) == 0
     assert ws(4, 100, 8, 2, 128, 16, 64, 64, 96) == 0            # not a multiple of 64
     assert _prefill_ex(lib, split=96) == 2                       # PA_ERR_BAD_SHAPE
     assert _prefill_ex(lib, split=-64) == 2
@@ -223,7 +226,7 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, NB=0) == 2
     assert _prefill(lib, scale=float("inf")) == 2
     assert _prefill(lib, dtype=0) == 3               # PA_ERR_UNSUPPORTED: f32
-    assert _prefill(lib, D=80) == 3
+    assert _prefill(lib, D=80, out=0) == 1          # head dim 80 accepted
     assert _prefill(lib, D=256) == 3
     assert _prefill(lib, D=64, out=0) == 1          # head dim 64 accepted
     assert _prefill(lib, BS=4) == 3

@@ -414,3 +414,42 @@ def test_prefill_head_dim_64_poison_and_bf16_p():
     g = oracle.storage_to_f64(Prefill(clean, dev).run(bf16_p=True), "bf16")
     assert np.linalg.norm(g - ref_r) / np.linalg.norm(ref_r) <= 4e-3
     assert np.max(np.abs(g - ref_r)) <= 1e-2 * vmax_of(clean)
+
+
+# head dim 80 (the 128-dim products on rows whose dims 80 .. 127 are zero in registers and LDS):
+# 16-bit types, GQA and MHA, 8-, 16-, 32- and 64-token blocks, whole prompts, split keys
+MATRIX_D80 = [
+    ("bf16", 16, 8, 2, (0, 5, 100, 37), (1, 17, 130, 64), 0),
+    ("f16", 32, 4, 4, (0, 90, 17), (40, 3, 100), 0),
+    ("bf16", 8, 8, 8, (0, 7, 101), (9, 64, 70), 0),
+    ("bf16", 64, 16, 2, (300, 1200), (77, 33), 128),
+    ("f16", 16, 2, 1, (0, 0), (300, 257), 0),
+]
+
+
+@pytest.mark.parametrize("dtype,bs,Hq,Hkv,prefix,chunk,kv_split", MATRIX_D80)
+def test_prefill_head_dim_80(dtype, bs, Hq, Hkv, prefix, chunk, kv_split):
+    dev = need_gpu()
+    case = W.build_prefill_case(_spec(dtype, bs, Hq, Hkv, prefix, chunk, seed=480 + sum(chunk), D=80))
+    say(f"prefill d80 {dtype} bs{bs} Hq{Hq} Hkv{Hkv} prefix={prefix} chunk={chunk} split={kv_split}")
+    got = Prefill(case, dev).run(kv_split=kv_split)
+    assert_attention_close(got, oracle_prefill(case), dtype, vmax_of(case), "prefill d80")
+
+
+def test_prefill_head_dim_80_poison_and_bf16_p():
+    """Head dim 80: NaN in unused slots and junk table entries change no bit (the padded dims are
+    never loaded); the output buffer's padding-free rows are written whole; the single-product
+    mode meets the bound of its one rounding."""
+    dev = need_gpu()
+    spec = _spec("bf16", 16, 16, 2, (0, 64, 300), (100, 64, 40), seed=81, D=80)
+    clean = W.build_prefill_case(spec)
+    say("prefill d80 poison + bf16_p")
+    a = Prefill(clean, dev).run()
+    b = Prefill(W.build_prefill_case(spec, poison=True, table_fill=2**31 - 1), dev).run(fill=0x7FC0)
+    assert np.array_equal(bits(a, "bf16"), bits(b, "bf16"))
+    ref = oracle_prefill(clean)
+    assert_attention_close(a, ref, "bf16", vmax_of(clean), "prefill d80 clean")
+    ref_r = oracle.storage_to_f64(oracle.f64_to_storage(ref, "bf16"), "bf16")
+    g = oracle.storage_to_f64(Prefill(clean, dev).run(bf16_p=True), "bf16")
+    assert np.linalg.norm(g - ref_r) / np.linalg.norm(ref_r) <= 4e-3
+    assert np.max(np.abs(g - ref_r)) <= 1e-2 * vmax_of(clean)

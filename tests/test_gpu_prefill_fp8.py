@@ -84,7 +84,7 @@ MATRIX = [
 ]
 
 
-@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("D", [128, 64, 80])
 @pytest.mark.parametrize("dtype,bs,Hq,Hkv,prefix,chunk,kv_split", MATRIX)
 def test_prefill_fp8_matches_oracle(dtype, bs, Hq, Hkv, prefix, chunk, kv_split, D):
     dev = need_gpu()
