@@ -595,6 +595,7 @@ def main(argv=None):
     ap.add_argument("--only", default="",
                     help="time only these detail legs (comma-separated: a decode workload, "
                          "prefill_llama7b, prefill_gqa, prefill_llama7b_fp8, prefill_gptoss_d64, "
+                         "prefill_d80, "
                          "swap_blocks, "
                          "device_engine, read_ceiling) "
                          "and print them")
@@ -738,7 +739,8 @@ def main(argv=None):
         torch.cuda.empty_cache()
         detail["read_ceiling"] = read_ceiling(dev, max(5, args.steps // 2))
         torch.cuda.empty_cache()
-        for pname in ("prefill_llama7b", "prefill_gqa", "prefill_llama7b_fp8", "prefill_gptoss_d64"):
+        for pname in ("prefill_llama7b", "prefill_gqa", "prefill_llama7b_fp8", "prefill_gptoss_d64",
+                      "prefill_d80"):
             detail[pname] = measure_prefill(dev, pname, args.steps, args.warmup)
         torch.cuda.empty_cache()
         detail["shared_prefix_device_engine"] = measure_device_engine(dev, args.steps, args.warmup)

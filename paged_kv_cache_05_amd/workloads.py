@@ -451,6 +451,10 @@ PREFILL_CONFIGS = {
     # attention shape): 512-token chunks on 0..1536 cached tokens
     "prefill_gptoss_d64": PrefillSpec("prefill_gptoss_d64", 8, 16, 64, 8, 64, "bf16", 16,
                                       ("uniform", 0, 1536), ("fixed", [512] * 16)),
+    # heads of 80 dims, which the kernel runs as 128-dim products on zero-padded rows: the
+    # Llama-7B-shaped prefill with 32 heads of 80 dims
+    "prefill_d80": PrefillSpec("prefill_d80", 9, 32, 32, 32, 80, "bf16", 16,
+                               ("uniform", 0, 1536), ("fixed", [512] * 32)),
     # the Llama-7B-shaped chunked prefill over an E4M3 cache
     "prefill_llama7b_fp8": PrefillSpec("prefill_llama7b_fp8", 6, 32, 32, 32, 128, "bf16", 16,
                                        ("uniform", 0, 1536), ("fixed", [512] * 32), kv_dtype="fp8"),
