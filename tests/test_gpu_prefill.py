@@ -193,13 +193,15 @@ def test_prefill_invalid_and_clamped_rows():
     assert np.array_equal(bits(got[:r3 + 32], "f16"), bits(base[:r3 + 32], "f16"))
 
 
-def test_prefill_full_size_sampled():
-    """The Llama-7B-shaped chunked-prefill workload (32 sequences, 512-token chunks on
-    0..1536 cached tokens, pools on the GPU), run as the benchmark runs it; sampled rows of
-    three sequences are checked against the oracle on one-row chunks."""
+@pytest.mark.parametrize("name", ["prefill_llama7b", "prefill_d80"])
+def test_prefill_full_size_sampled(name):
+    """The Llama-7B-shaped chunked-prefill workloads (32 sequences, 512-token chunks on
+    0..1536 cached tokens, pools on the GPU; heads of 128 and of 80 dims), run as the benchmark
+    runs them; sampled rows of three sequences are checked against the oracle on one-row
+    chunks."""
     import torch
     dev = need_gpu()
-    spec = W.PREFILL_CONFIGS["prefill_llama7b"]
+    spec = W.PREFILL_CONFIGS[name]
     case = W.build_prefill_case(spec, device=dev)
     say(f"prefill full size: {spec.name}, pool {case.pool.num_blocks} blocks")
     got = Prefill(case, dev).run()
