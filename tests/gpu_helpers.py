@@ -207,3 +207,40 @@ def compare_every_sequence(case: W.DecodeCase, got, kc, vc, snaps, oracle_seq, w
     say(f"  {what}: {S} sequences compared; largest error in sequence {worst} "
         f"(n={int(case.context_lens[worst])})")
     return assert_attention_close(got, ref, out_dt, vmax, f"{what} (all {S} sequences)")
+
+
+def prefill_every_row(case, got, dev, what, pool_dtype, ref_fn, vmax_fn):
+    """Every row of every sequence of a prefill run against the oracle.  Each sequence's blocks
+    are copied to the host (``pool_dtype`` storage) and given to ``ref_fn(query rows, keys,
+    values, table, query_start_loc, context_lens)`` as a sequence of its own (table 0 .. nb-1);
+    sequences run in a pool of host threads.  ``vmax_fn(values)`` gives max|V| for the bar."""
+    import concurrent.futures as cf
+    import torch
+    from threadpoolctl import threadpool_limits
+    bs = case.block_size
+    ref = np.zeros(got.shape, dtype=np.float64)
+    vmax = 0.0
+
+    def one(s, kc, vc):
+        n, L = int(case.context_lens[s]), int(case.query_lens[s])
+        q0 = int(case.query_start_loc[s])
+        table = np.arange(kc.shape[0], dtype=np.int32)[None]
+        out = ref_fn(case.query[q0:q0 + L], kc, vc, table, np.array([0, L], np.int32),
+                     np.array([n], np.int32))
+        return q0, L, out, vmax_fn(vc)
+
+    S = case.spec.num_seqs
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        futs = []
+        for s in range(S):
+            nb = -(-int(case.context_lens[s]) // bs)
+            ids = torch.from_numpy(case.pool.block_tables[s, :nb].astype(np.int64)).to(dev)
+            kc = W.from_torch(case.pool.key_cache.index_select(0, ids), pool_dtype)
+            vc = W.from_torch(case.pool.value_cache.index_select(0, ids), pool_dtype)
+            futs.append(ex.submit(one, s, kc, vc))
+        for f in futs:
+            q0, L, out, vm = f.result()
+            ref[q0:q0 + L] = out
+            vmax = max(vmax, vm)
+    say(f"  {what}: every row of {S} sequences compared")
+    return assert_attention_close(got, ref, case.dtype, vmax, f"{what}: every row of {S} sequences")

@@ -16,7 +16,7 @@ import oracle
 from paged_kv_cache_05_amd import ops
 from paged_kv_cache_05_amd import workloads as W
 
-from gpu_helpers import assert_attention_close, bits, need_gpu, say
+from gpu_helpers import assert_attention_close, bits, need_gpu, prefill_every_row, say
 
 pytestmark = pytest.mark.gpu
 
@@ -193,38 +193,29 @@ def test_prefill_invalid_and_clamped_rows():
     assert np.array_equal(bits(got[:r3 + 32], "f16"), bits(base[:r3 + 32], "f16"))
 
 
+def _ref_16bit(case):
+    """The oracle on one sequence's rows over its own blocks (16-bit pools)."""
+    def ref(q, kc, vc, table, qsl, ctx):
+        return oracle.prefill_ref(q, kc, vc, table, qsl, ctx, case.block_size, case.scale, case.dtype)
+    return ref
+
+
+def _vmax_16bit(case):
+    return lambda vc: float(np.max(np.abs(oracle.storage_to_f64(vc, case.dtype))))
+
+
 @pytest.mark.parametrize("name", ["prefill_llama7b", "prefill_d80"])
-def test_prefill_full_size_sampled(name):
+def test_prefill_full_size_every_row(name):
     """The Llama-7B-shaped chunked-prefill workloads (32 sequences, 512-token chunks on
     0..1536 cached tokens, pools on the GPU; heads of 128 and of 80 dims), run as the benchmark
-    runs them; sampled rows of three sequences are checked against the oracle on one-row
-    chunks."""
-    import torch
+    runs them; every row of every sequence against the oracle."""
     dev = need_gpu()
     spec = W.PREFILL_CONFIGS[name]
     case = W.build_prefill_case(spec, device=dev)
     say(f"prefill full size: {spec.name}, pool {case.pool.num_blocks} blocks")
     got = Prefill(case, dev).run()
     assert np.all(np.isfinite(oracle.storage_to_f64(got, "bf16")))
-    rng = np.random.default_rng(13)
-    bs = spec.block_size
-    for s in (0, 17, 31):
-        n = int(case.context_lens[s])
-        L = int(case.query_lens[s])
-        nb = -(-n // bs)
-        ids = torch.from_numpy(case.pool.block_tables[s, :nb].astype(np.int64)).to(dev)
-        kc = W.from_torch(case.pool.key_cache.index_select(0, ids), "bf16")
-        vc = W.from_torch(case.pool.value_cache.index_select(0, ids), "bf16")
-        table = np.arange(nb, dtype=np.int32)[None]
-        rows = np.sort(rng.choice(L, size=24, replace=False))
-        rows[0], rows[-1] = 0, L - 1
-        q0 = int(case.query_start_loc[s])
-        vmax = float(np.max(np.abs(oracle.storage_to_f64(vc, "bf16"))))
-        for i in rows:
-            ref = oracle.prefill_ref(case.query[q0 + i:q0 + i + 1], kc, vc, table,
-                                     np.array([0, 1], np.int32),
-                                     np.array([n - L + i + 1], np.int32), bs, case.scale, "bf16")
-            assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
+    prefill_every_row(case, got, dev, name, case.dtype, _ref_16bit(case), _vmax_16bit(case))
 
 
 def test_prefill_long_chunks_sampled():
@@ -328,35 +319,17 @@ def test_prefill_library_split_choice():
                            "library split")
 
 
-def test_prefill_gqa_full_size_sampled():
+def test_prefill_gqa_full_size_every_row():
     """The GQA chunked-prefill workload (8 sequences, ragged chunks on up to 3000 cached
-    tokens), run as the benchmark runs it (the library splits its keys); sampled rows of
-    three sequences against the oracle on one-row chunks."""
-    import torch
+    tokens), run as the benchmark runs it (the library splits its keys); every row of every
+    sequence against the oracle."""
     dev = need_gpu()
     spec = W.PREFILL_CONFIGS["prefill_gqa"]
     case = W.build_prefill_case(spec, device=dev)
     say(f"prefill full size: {spec.name}")
     got = Prefill(case, dev).run()
     assert np.all(np.isfinite(oracle.storage_to_f64(got, "bf16")))
-    rng = np.random.default_rng(25)
-    bs = spec.block_size
-    for s in (0, 3, 7):
-        n = int(case.context_lens[s])
-        L = int(case.query_lens[s])
-        nb = -(-n // bs)
-        ids = torch.from_numpy(case.pool.block_tables[s, :nb].astype(np.int64)).to(dev)
-        kc = W.from_torch(case.pool.key_cache.index_select(0, ids), "bf16")
-        vc = W.from_torch(case.pool.value_cache.index_select(0, ids), "bf16")
-        table = np.arange(nb, dtype=np.int32)[None]
-        rows = np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=min(L, 12), replace=False)]))
-        q0 = int(case.query_start_loc[s])
-        vmax = float(np.max(np.abs(oracle.storage_to_f64(vc, "bf16"))))
-        for i in rows:
-            ref = oracle.prefill_ref(case.query[q0 + i:q0 + i + 1], kc, vc, table,
-                                     np.array([0, 1], np.int32),
-                                     np.array([n - L + i + 1], np.int32), bs, case.scale, "bf16")
-            assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
+    prefill_every_row(case, got, dev, "prefill_gqa", case.dtype, _ref_16bit(case), _vmax_16bit(case))
 
 
 def test_plain_pa_prefill_entry():

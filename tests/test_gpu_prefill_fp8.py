@@ -15,7 +15,7 @@ import oracle
 from paged_kv_cache_05_amd import ops
 from paged_kv_cache_05_amd import workloads as W
 
-from gpu_helpers import assert_attention_close, bits, need_gpu, say
+from gpu_helpers import assert_attention_close, bits, need_gpu, prefill_every_row, say
 
 pytestmark = pytest.mark.gpu
 
@@ -128,33 +128,21 @@ def test_prefill_fp8_bad_scales():
     torch.cuda.synchronize()
 
 
-def test_prefill_fp8_full_size_sampled():
+def test_prefill_fp8_full_size_every_row():
     """The Llama-7B-shaped chunked prefill over an E4M3 cache (32 x 512-token chunks on 0..1536
-    cached tokens), as the benchmark runs it; sampled rows of three sequences against the
-    oracle on one-row chunks."""
-    import torch
+    cached tokens), as the benchmark runs it; every row of every sequence against the oracle
+    on the dequantized pools."""
     dev = need_gpu()
     spec = W.PREFILL_CONFIGS["prefill_llama7b_fp8"]
     case = W.build_prefill_case(spec, device=dev)
     say(f"prefill full size: {spec.name}")
     got = Run(case, dev)()
     assert np.all(np.isfinite(oracle.storage_to_f64(got, "bf16")))
-    rng = np.random.default_rng(33)
-    bs = spec.block_size
-    for s in (0, 15, 31):
-        n = int(case.context_lens[s])
-        L = int(case.query_lens[s])
-        nb = -(-n // bs)
-        ids = torch.from_numpy(case.pool.block_tables[s, :nb].astype(np.int64)).to(dev)
-        kc = W.from_torch(case.pool.key_cache.index_select(0, ids), "fp8")
-        vc = W.from_torch(case.pool.value_cache.index_select(0, ids), "fp8")
-        table = np.arange(nb, dtype=np.int32)[None]
-        rows = np.unique(np.concatenate([[0, L - 1], rng.choice(L, size=min(L, 10), replace=False)]))
-        q0 = int(case.query_start_loc[s])
-        vmax = float(np.max(np.abs(oracle.dequantize_fp8(vc, V_SCALE))))
-        for i in rows:
-            ref = oracle.prefill_fp8_ref(case.query[q0 + i:q0 + i + 1], kc, vc, table,
-                                         np.array([0, 1], np.int32),
-                                         np.array([n - L + i + 1], np.int32), bs, case.scale,
-                                         "bf16", K_SCALE, V_SCALE)
-            assert_attention_close(got[q0 + i:q0 + i + 1], ref, "bf16", vmax, f"seq {s} row {i}")
+
+    def ref(q, kc, vc, table, qsl, ctx):
+        return oracle.prefill_fp8_ref(q, kc, vc, table, qsl, ctx, case.block_size, case.scale,
+                                      "bf16", K_SCALE, V_SCALE)
+
+    prefill_every_row(case, got, dev, spec.name, "fp8", ref,
+                      lambda vc: float(np.max(np.abs(oracle.dequantize_fp8(vc, V_SCALE)))))
+
