@@ -204,11 +204,12 @@ def _vmax_16bit(case):
     return lambda vc: float(np.max(np.abs(oracle.storage_to_f64(vc, case.dtype))))
 
 
-@pytest.mark.parametrize("name", ["prefill_llama7b", "prefill_d80"])
+@pytest.mark.parametrize("name", ["prefill_llama7b", "prefill_d80", "prefill_gptoss_d64"])
 def test_prefill_full_size_every_row(name):
-    """The Llama-7B-shaped chunked-prefill workloads (32 sequences, 512-token chunks on
-    0..1536 cached tokens, pools on the GPU; heads of 128 and of 80 dims), run as the benchmark
-    runs them; every row of every sequence against the oracle."""
+    """The chunked-prefill workloads with 512-token chunks on 0..1536 cached tokens (pools on
+    the GPU): Llama-7B-shaped with heads of 128 and of 80 dims, and GPT-OSS-shaped (16 sequences,
+    64 query / 8 KV heads of 64 dims), run as the benchmark runs them; every row of every
+    sequence against the oracle."""
     dev = need_gpu()
     spec = W.PREFILL_CONFIGS[name]
     case = W.build_prefill_case(spec, device=dev)
