@@ -458,7 +458,7 @@ def pin_prefill_sdpa_causal(O):
     """A whole prompt prefilled at once (no prefix) equals torch's float64 causal SDPA
     (``is_causal=True``, torch's own mask) on the contiguous K/V, with GQA."""
     for i, (dtype, bs, d, Hq, Hkv) in enumerate((("f32", 16, 16, 4, 2), ("bf16", 32, 32, 6, 3),
-                                                  ("f16", 16, 64, 2, 2))):
+                                                  ("f16", 16, 64, 2, 2), ("bf16", 16, 80, 4, 1))):
         c = _pcase(S=3, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, bs=bs, prefix=(0, 0, 0),
                    chunk=(1, bs + 3, 2 * bs + 1), seed=50 + i)
         out = _prun(O, c)
