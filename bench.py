@@ -95,9 +95,9 @@ def cache_write_bytes(case) -> int:
 def chosen_kernel(case, requested: str) -> str:
     sp = case.spec
     G = sp.num_heads // sp.num_kv_heads
-    grouped = sp.dtype in ("f16", "bf16") and sp.head_dim in (64, 128, 256) and G % 4 == 0
+    grouped = sp.dtype in ("f16", "bf16") and sp.head_dim in (64, 80, 128, 256) and G % 4 == 0
     if sp.kv_dtype == "fp8":
-        return "mfma_fp8" if grouped and sp.head_dim == 128 else "valu_fp8"
+        return "mfma_fp8" if grouped else "valu_fp8"
     if requested != "auto":
         return requested
     return "mfma" if grouped else "valu"

@@ -111,7 +111,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   out[s][h] = sum_t softmax(z)_t * V_t          (softmax evaluated stably, shifted by a
  *                                                   running maximum; fp32 accumulation)
  * and out[s][h] = 0 when n <= 0.  pa_decode runs the matrix-core kernel when dtype is
- * PA_F16/PA_BF16, head_dim is 64, 128 or 256 and G is a multiple of 4, and the vector-ALU kernel
+ * PA_F16/PA_BF16, head_dim is 64, 80, 128 or 256 (80: the 128-dim products with dims 80 .. 127
+ * held as zeros, never loaded or stored) and G is a multiple of 4, and the vector-ALU kernel
  * otherwise (arithmetic of each: see the element-type note at the top).  Paging changes where K/V live, not the result (the
  * xasun.com summary, section 一, calls the scheme lossless).
  *
@@ -148,7 +149,7 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
 
 /*
  * pa_decode_ex — pa_decode with an explicit kernel family and flags.  PA_KERNEL_MFMA
- * requires dtype f16/bf16, head_dim 64, 128 or 256 and num_heads / num_kv_heads a multiple of 4
+ * requires dtype f16/bf16, head_dim 64, 80, 128 or 256 and num_heads / num_kv_heads a multiple of 4
  * (PA_ERR_UNSUPPORTED otherwise); PA_KERNEL_VALU accepts every supported shape.  `flags` is
  * a combination of PA_DECODE_* bits (unknown bits: PA_ERR_UNSUPPORTED).  Same arguments,
  * results and errors as pa_decode otherwise.
@@ -368,7 +369,7 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key
  * (pa_decode_workspace_bytes with the same sizes), flags and errors as pa_decode_ex.
  * pa_decode_fp8_partitions is its first launch (pa_decode_merge, with the same dtype, is the
  * second).  Supported: head_dim 64, 80, 128 or 256, block_size 8, 16, 32, 64 or 128.  When
- * head_dim is 64, 128 or 256 and num_heads / num_kv_heads is a multiple of 4 (and partition_size
+ * head_dim is 64, 80, 128 or 256 and num_heads / num_kv_heads is a multiple of 4 (and partition_size
  * one of 16) the grouped heads run on the matrix cores, the codes converted exactly to dtype in
  * registers; otherwise on the vector ALUs.
  */

@@ -40,6 +40,7 @@ COMMON_FLAGS = [
 EXTRA_FLAGS = {
     "pa_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "pa_decode_mfma_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "pa_decode_mfma_d80.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

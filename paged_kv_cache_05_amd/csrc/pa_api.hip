@@ -95,9 +95,11 @@ Plan make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, int32_
 }
 
 bool mfma_eligible(DT dt, int D, int G, int partition) {
-  return (dt == DT::F16 || dt == DT::BF16) && (D == 64 || D == 128 || D == 256) && G % 4 == 0 &&
-         partition % 16 == 0;
+  return (dt == DT::F16 || dt == DT::BF16) && (D == 64 || D == 80 || D == 128 || D == 256) &&
+         G % 4 == 0 && partition % 16 == 0;
 }
+// Head dim of the matrix-core products: 80-dim heads run through the 128-dim ones (padded).
+int mfma_compute_dim(int D) { return D == 80 ? 128 : D; }
 
 // Consecutive partitions one matrix-core workgroup walks.  Walking several pays the query and
 // table prologue once per workgroup instead of once per partition, and each partition still
@@ -296,7 +298,7 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
   p.v_scale = 1.0f;
 
   const long units = (long)num_seqs * num_kv_heads * p.head_chunks;
-  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt, head_dim) : 1;
+  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt, mfma_compute_dim(head_dim)) : 1;
   const long grid = mfma ? units * ((pl.max_parts + p.parts_per_wg - 1) / p.parts_per_wg)
                         : valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;
@@ -652,7 +654,7 @@ pa_status pa_decode_fp8_partitions(void* out, const void* query, const void* key
   p.scale_log2 = scale * k_scale * 1.4426950408889634f;
   p.v_scale = v_scale;
   const long units = (long)num_seqs * num_kv_heads * p.head_chunks;
-  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt, head_dim) : 1;
+  p.parts_per_wg = mfma ? mfma_parts_per_wg(pl.partition, pl.max_parts, units, gt, mfma_compute_dim(head_dim)) : 1;
   const long grid = mfma ? units * ((pl.max_parts + p.parts_per_wg - 1) / p.parts_per_wg)
                         : valu_grid(num_seqs, num_kv_heads, p.head_chunks, pl.max_parts);
   if (grid > 0x7FFFFFFFL) return PA_ERR_BAD_SHAPE;

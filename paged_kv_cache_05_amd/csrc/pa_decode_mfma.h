@@ -191,9 +191,15 @@ constexpr int mfma_slots(int gt, int d) { return 2048 / (gt * d) >= 4 ? 4 : 2048
 // the shorter 8-bit chunks.  The 16-bit instances are built with their MFMA accumulators in
 // ordinary VGPRs (176-180 registers, two waves per SIMD); asked for three waves they spill 7-10
 // values and ran GQA long-context batches 13% slower.
-template <DT dt, DT kt, int D, int BS, int GT, bool STREAM>
+// DP: the head dim of the queries, outputs and pools.  It equals D, except for heads of 80 dims,
+// which run through the 128-dim products (D = 128, DP = 80) with dims 80 .. 127 zero in
+// registers and LDS: they are never loaded or stored, add nothing to a score and give output
+// dims that are dropped.
+template <DT dt, DT kt, int D, int BS, int GT, bool STREAM, int DP = D>
 __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel(const DecodeParams p) {
   static_assert(D == 64 || D == 128 || D == 256, "head dim");
+  static_assert(DP == D || (D == 128 && DP == 80), "stored head dim: as computed, or 80 in 128");
+  constexpr bool PAD = DP != D;
   constexpr int EB = 2;            // query / output element bytes
   constexpr bool K8 = kt == DT::FP8;
   constexpr int EBK = K8 ? 1 : 2;  // cache element bytes
@@ -205,7 +211,13 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   constexpr int TPL = 1024 / ROW;  // token rows per K load
   constexpr int LPR = ROW / 16;    // lanes per token row in a K load
   constexpr int VW = DPL * EBK / 4;     // 32-bit words of this lane's piece of a V row
-  using Chunk = ChunkBuf<NK, VW>;
+  // Stored rows (PAD): ROWP bytes, a chunk's 16 K rows one contiguous run of 16 ROWP bytes
+  // loaded as 16-byte pieces (PPR a row), NKL loads of 64 pieces, the last one partial.
+  constexpr int ROWP = DP * EBK;
+  constexpr int PPR = ROWP / 16;
+  constexpr int NKL = PAD ? (16 * PPR + 63) / 64 : NK;
+  constexpr int KCE = PAD ? (DP + 31) / 32 : KC;   // depth steps that hold stored dims
+  using Chunk = ChunkBuf<NKL, VW>;
   constexpr int CPB = BS >= 16 ? BS / 16 : 1;   // 16-token chunks per block
   constexpr int BPC = BS >= 16 ? 1 : 16 / BS;   // blocks per chunk (2 for 8-token blocks)
   static_assert(BS % 16 == 0 || BS == 8, "block size must be 8 or a multiple of 16");
@@ -237,15 +249,21 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   // Loads independent of the context length first (their latency overlaps the read of
   // context_lens): the Q^T operand and the table entries of this wave's first 64 chunks
   // (entries past the sequence's end are loaded but never used; all lie inside the row).
-  const size_t q_row0 = ((size_t)s * p.num_heads + h0) * D;
+  const size_t q_row0 = ((size_t)s * p.num_heads + h0) * DP;
   const int32_t* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const int ch_begin = p0 * (p.partition / 16);
   uint4 qb[KC];  // Q^T operand (unscaled 16-bit values): chunk kc holds Q[h][32kc + 8kg .. +8]
   {
-    const char* qp = (const char*)p.q + (q_row0 + (size_t)(lr % GT) * D) * EB;
+    const char* qp = (const char*)p.q + (q_row0 + (size_t)(lr % GT) * DP) * EB;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
+    for (int kc = 0; kc < KC; ++kc) {
+      if constexpr (PAD)
+        qb[kc] = kc < KCE && 32 * kc + 8 * kg < DP
+                     ? *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB)
+                     : make_uint4(0, 0, 0, 0);
+      else
+        qb[kc] = *reinterpret_cast<const uint4*>(qp + (32 * kc + 8 * kg) * EB);
+    }
   }
   // table entries of chunk ch: its block, or its two 8-token blocks (the second lies past the
   // table row when the row length is odd)
@@ -265,7 +283,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   const int nparts = n > 0 ? (n + p.partition - 1) / p.partition : 1;
   if (p0 >= nparts) return;
   if (n <= 0) {  // empty context: the output is defined as zero
-    if (threadIdx.x < GT * D / 8)
+    if (threadIdx.x < GT * DP / 8)
       *reinterpret_cast<uint4*>((char*)p.out + (q_row0 * EB) + threadIdx.x * 16) =
           make_uint4(0, 0, 0, 0);
     return;
@@ -281,9 +299,10 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   const int t_end = min(n, (p0 + np_wg) * p.partition);
   const int ch_end = (t_end + 15) / 16;
   const int Q = p.partition / 64;   // a wave's chunks in each full partition (used if np_wg > 1)
-  const size_t head_off = (size_t)g * BS * D;
-  const size_t block_stride = (size_t)p.num_kv_heads * BS * D;
-  const int v_off = (4 * kg * D + DPL * lr) * EBK;   // V rows: token 4kg (+j), dims DPL lr ..
+  const size_t head_off = (size_t)g * BS * DP;
+  const size_t block_stride = (size_t)p.num_kv_heads * BS * DP;
+  const int v_off = (4 * kg * DP + DPL * lr) * EBK;   // V rows: token 4kg (+j), dims DPL lr ..
+  const bool v_live = !PAD || DPL * lr < DP;          // this lane's V dims are stored ones
 
   // K arrives coalesced (load i, lane l: token TPL i + l / LPR, 16-byte piece l % LPR -- each
   // load instruction reads whole rows) and is re-laid out through a wave-private LDS tile of 16
@@ -295,9 +314,16 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   __shared__ uint4 s_k[4][16 * KCOL];
   uint4* kst = s_k[wave];
   auto kslot = [](int t, int c) { return KCOL * t + (c ^ (KCOL >= 16 ? t : t >> 1)); };
+  if constexpr (PAD) {
+    // columns DP / 8 .. 4 KCE - 1 are read by the last depth step but hold no stored dims:
+    // zero them once (the wave's own tile; nothing else writes them)
+    constexpr int ZC = 4 * KCE - DP / 8;
+    for (int z = lane; z < 16 * ZC; z += kWave)
+      kst[kslot(z & 15, DP / 8 + z / 16)] = make_uint4(0, 0, 0, 0);
+  }
 
   auto load_chunk = [&](Chunk& c, int phys0, int phys1, int ch) {
-    const size_t el0 = (size_t)phys0 * block_stride + head_off + (size_t)(ch % CPB) * 16 * D;
+    const size_t el0 = (size_t)phys0 * block_stride + head_off + (size_t)(ch % CPB) * 16 * DP;
     // K: load i reads 1 KiB = TPL token rows, lane l 16 bytes of it
     const char* kp0 = (const char*)p.kc + el0 * EBK + lane * 16;
     const char* kp1 = kp0;
@@ -305,14 +331,34 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     if constexpr (BPC == 2) {
       // tokens 0-7 in block phys0, 8-15 in phys1 (at offsets 0-7 there)
       const size_t el1 = (size_t)phys1 * block_stride + head_off;
-      kp1 = (const char*)p.kc + el1 * EBK + lane * 16 - 8 * ROW;
-      if (kg >= 2) vp = (const char*)p.vc + el1 * EBK + v_off - 8 * ROW;
+      kp1 = (const char*)p.kc + el1 * EBK + lane * 16 - 8 * ROWP;
+      if (kg >= 2) vp = (const char*)p.vc + el1 * EBK + v_off - 8 * ROWP;
     }
+    if constexpr (PAD) {
+      // piece q = 64 i + lane of the chunk's 16 contiguous stored rows: token q / PPR; pieces
+      // past the 16 rows are not loaded
 #pragma unroll
-    for (int i = 0; i < NK; ++i)   // token TPL i + lane / LPR: tokens 8-15 of an 8-token pair in phys1
-      c.k[i] = load_kv<STREAM>((TPL * i + lane / LPR < 8 ? kp0 : kp1) + 1024 * i);
+      for (int i = 0; i < NKL; ++i) {
+        const int q = 64 * i + lane;
+        c.k[i] = make_uint4(0, 0, 0, 0);
+        if (q < 16 * PPR) c.k[i] = load_kv<STREAM>((q / PPR < 8 ? kp0 : kp1) + 1024 * i);
+      }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_words<VW, STREAM>(c.v[j], vp + j * ROW);
+      for (int j = 0; j < 4; ++j) {
+        if (v_live) {
+          load_words<VW, STREAM>(c.v[j], vp + j * ROWP);
+        } else {
+#pragma unroll
+          for (int w = 0; w < VW; ++w) c.v[j][w] = 0;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i)   // token TPL i + lane / LPR: tokens 8-15 of an 8-token pair in phys1
+        c.k[i] = load_kv<STREAM>((TPL * i + lane / LPR < 8 ? kp0 : kp1) + 1024 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_words<VW, STREAM>(c.v[j], vp + j * ROW);
+    }
   };
   // End of partition p0 + k for this wave: it leaves its state (running max, denominator,
   // unnormalised outputs) in the partition's LDS slot and starts the next partition afresh.
@@ -363,7 +409,25 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   // lane's tokens 4kg .. 4kg+3 lie in block kg/2 of an 8-token pair
   auto consume = [&](Chunk& c, int ch, int okm) {
     const bool ok = ((okm >> (BPC == 1 ? 0 : kg >> 1)) & 1) != 0;
-    if constexpr (K8) {
+    if constexpr (PAD) {
+      // piece q = 64 i + lane: token q / PPR, 16 bytes at q % PPR of its stored row -- 8
+      // 16-bit dims (column q % PPR), or 16 codes that become columns 2 (q % PPR) and +1
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) {
+        const int q = 64 * i + lane;
+        if (q < 16 * PPR) {
+          const int t = q / PPR, j = q % PPR;
+          if constexpr (K8) {
+            const uint2 a = fp8x4_to_16bit<M>(c.k[i].x), b = fp8x4_to_16bit<M>(c.k[i].y);
+            const uint2 d = fp8x4_to_16bit<M>(c.k[i].z), e = fp8x4_to_16bit<M>(c.k[i].w);
+            kst[kslot(t, 2 * j)] = make_uint4(a.x, a.y, b.x, b.y);
+            kst[kslot(t, 2 * j + 1)] = make_uint4(d.x, d.y, e.x, e.y);
+          } else {
+            kst[kslot(t, j)] = c.k[i];
+          }
+        }
+      }
+    } else if constexpr (K8) {
       // lane l of load i holds 16 codes: token TPL i + l / LPR, dims 16 (l % LPR) .. +15, which
       // become the 16-bit columns 2 (l % LPR) and 2 (l % LPR) + 1 of that token
 #pragma unroll
@@ -378,12 +442,12 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
 #pragma unroll
       for (int i = 0; i < NK; ++i) kst[kslot(TPL * i + lane / LPR, lane % LPR)] = c.k[i];
     }
-    uint4 kop[KC];
+    uint4 kop[KCE];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) kop[kc] = kst[kslot(lr, 4 * kc + kg)];
+    for (int kc = 0; kc < KCE; ++kc) kop[kc] = kst[kslot(lr, 4 * kc + kg)];
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) st = M::mma32(kop[kc], qb[kc], st);
+    for (int kc = 0; kc < KCE; ++kc) st = M::mma32(kop[kc], qb[kc], st);
     const int tok0 = ch * 16 + 4 * kg;   // token of register j is tok0 + j
     const bool full = okm == 3 && (ch * 16 + 16 <= t_end);
     float sv[4];
@@ -544,7 +608,7 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
   before = __builtin_amdgcn_readfirstlane(before);
   if (before != 3) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  constexpr int CPH = D / 8;   // 8-dim pieces of a head's output
+  constexpr int CPH = DP / 8;   // 8-dim pieces of a head's (stored) output
   for (int t = lane; t < np_wg * GT * CPH; t += kWave) {
     const int k = t / (GT * CPH), h = (t / CPH) % GT, cc = t % CPH;
     float Mx = s_m[k][0][h];
@@ -563,12 +627,12 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
     const float inv = p.v_scale / L;   // an 8-bit cache's value scale factors out of the sum
 #pragma unroll
     for (int e = 0; e < 8; ++e) O[e] *= inv;
-    const size_t qrow = q_row0 + (size_t)h * D;
+    const size_t qrow = q_row0 + (size_t)h * DP;
     if (nparts == 1) {
       *reinterpret_cast<uint4*>((char*)p.out + (qrow + cc * 8) * EB) = Elem<dt>::pack(O);
     } else {
       const size_t slot = ((size_t)s * p.num_heads + h0 + h) * p.max_parts + p0 + k;
-      float* po = p.ws_o + slot * D + cc * 8;
+      float* po = p.ws_o + slot * DP + cc * 8;
       store_stream(po, O[0], O[1], O[2], O[3]);
       store_stream(po + 4, O[4], O[5], O[6], O[7]);
       if (cc == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(Mx, L);
@@ -579,17 +643,17 @@ __global__ __launch_bounds__(256, kt == DT::FP8 ? 3 : 1) void decode_mfma_kernel
 
 
 
-template <DT dt, DT kt, int D, int BS, bool ST>
+template <DT dt, DT kt, int D, int BS, bool ST, int DP = D>
 hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
   // the kernel holds LDS slots for mfma_slots(gt, D) partitions (and 16 heads need D <= 128)
   if (gt * D > 2048 || p.parts_per_wg < 1 || p.parts_per_wg > mfma_slots(gt, D))
     return hipErrorInvalidValue;
   switch (gt) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 4, ST>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 8, ST>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 4, ST, DP>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 8, ST, DP>), dim3(grid), dim3(256), 0, st, p); break;
     case 16:
       if constexpr (D <= 128) {
-        hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 16, ST>), dim3(grid), dim3(256), 0, st, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<dt, kt, D, BS, 16, ST, DP>), dim3(grid), dim3(256), 0, st, p);
         break;
       }
       return hipErrorInvalidValue;
@@ -598,11 +662,11 @@ hipError_t launch_gt(int gt, const DecodeParams& p, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <DT dt, DT kt, int D>
+template <DT dt, DT kt, int D, int DP = D>
 hipError_t launch_bs(int bs, int gt, bool sk, const DecodeParams& p, int grid, hipStream_t st) {
   auto go = [&](auto bs_tag) -> hipError_t {
     constexpr int BS = decltype(bs_tag)::value;
-    return sk ? launch_gt<dt, kt, D, BS, true>(gt, p, grid, st) : launch_gt<dt, kt, D, BS, false>(gt, p, grid, st);
+    return sk ? launch_gt<dt, kt, D, BS, true, DP>(gt, p, grid, st) : launch_gt<dt, kt, D, BS, false, DP>(gt, p, grid, st);
   };
   switch (bs) {
     case 8: return go(std::integral_constant<int, 8>{});

@@ -70,7 +70,7 @@ def test_decode_argument_errors(lib):
     assert _decode(lib, kernel=9) == 3
     assert _decode(lib, kernel=2, dtype=0) == 3      # matrix-core path needs f16/bf16
     assert _decode(lib, kernel=2, Hq=6, Hkv=3) == 3  # group of 2
-    assert _decode(lib, kernel=2, D=80) == 3         # matrix cores: head dims 64, 128, 256
+    assert _decode(lib, kernel=2, D=80, out=0) == 1  # matrix cores: head dims 64, 80, 128, 256
     assert _decode(lib, kernel=2, D=64, out=0) == 1
     assert _decode(lib, kernel=2, D=256, out=0) == 1
     assert _decode(lib, flags=0x2) == 3              # unknown flag bit

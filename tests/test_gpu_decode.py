@@ -27,7 +27,7 @@ def _case(dtype, D, BS, Hq, Hkv, lengths=EDGE_LENGTHS, seed=100, **kw):
 
 
 def _mfma_ok(dtype, D, Hq, Hkv, P):
-    return dtype in ("f16", "bf16") and D in (64, 128, 256) and (Hq // Hkv) % 4 == 0 and P % 16 == 0
+    return dtype in ("f16", "bf16") and D in (64, 80, 128, 256) and (Hq // Hkv) % 4 == 0 and P % 16 == 0
 
 
 def _decode_matrix():
@@ -116,13 +116,14 @@ def test_head_dims_80_256(dtype, D, BS, heads):
 
 @pytest.mark.parametrize("heads", [(8, 2), (16, 2), (32, 2)])
 @pytest.mark.parametrize("BS", [8, 16, 64])
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 80, 256])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_mfma_head_dims_64_256(dtype, D, BS, heads):
-    """The matrix-core kernel at head dims 64 (8 LDS columns per K row, 4 output dims per lane)
-    and 256 (32 columns, 16 dims per lane, at most 8 heads per workgroup) with 4, 8 and 16 query
-    heads per KV head, single pass and split, against the oracle; NaN in every unread slot and
-    junk in unused table entries change no bit."""
+def test_mfma_head_dims_64_80_256(dtype, D, BS, heads):
+    """The matrix-core kernel at head dims 64 (8 LDS columns per K row, 4 output dims per lane),
+    80 (the 128-dim products on zero-padded rows: 160-byte rows loaded as 16-byte pieces, lanes
+    of dims 80 and up idle) and 256 (32 columns, 16 dims per lane, at most 8 heads per
+    workgroup) with 4, 8 and 16 query heads per KV head, single pass and split, against the
+    oracle; NaN in every unread slot and junk in unused table entries change no bit."""
     dev = need_gpu()
     Hq, Hkv = heads
     lengths = [1, 15, 16, 17, 65, 300, 1000]
