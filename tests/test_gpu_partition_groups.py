@@ -43,6 +43,7 @@ SHAPES = [
     (32, 8, 64, 1664, 128, 64),     # head dim 64, 4 heads -> 4
     (64, 8, 64, 1664, 128, 64),     # head dim 64, 8 heads -> 4
     (32, 8, 64, 1664, 128, 256),    # head dim 256, 4 heads -> 2
+    (32, 8, 64, 1664, 128, 80),     # head dim 80 (128-dim products), 4 heads -> 4
 ]
 
 
