@@ -132,6 +132,12 @@ CONFIGS = {
     # the GQA long-context step over an 8-bit E4M3 cache
     "gqa_long_fp8": CaseSpec("gqa_long_fp8", 4, 16, 32, 8, 128, "bf16", 16, ("uniform", 8192, 32768),
                              partition_size=512, kv_dtype="fp8"),
+    # the GQA long-context step with heads of 80 dims (16-bit and E4M3 caches), which the
+    # matrix-core kernel runs as 128-dim products on zero-padded rows
+    "gqa_long_d80": CaseSpec("gqa_long_d80", 4, 16, 32, 8, 80, "bf16", 16, ("uniform", 8192, 32768),
+                             partition_size=512),
+    "gqa_long_fp8_d80": CaseSpec("gqa_long_fp8_d80", 4, 16, 32, 8, 80, "bf16", 16,
+                                 ("uniform", 8192, 32768), partition_size=512, kv_dtype="fp8"),
 }
 
 
