@@ -53,24 +53,25 @@ def test_noalloc_refuses_oversized_partials():
                     0, 0, None) == 1             # null output
 
 
-def _case(seed, lengths, Hq, Hkv, dtype="bf16", bs=16):
-    return W.build_case(W.CaseSpec("noalloc", seed, len(lengths), Hq, Hkv, 128, dtype, bs,
+def _case(seed, lengths, Hq, Hkv, dtype="bf16", bs=16, D=128):
+    return W.build_case(W.CaseSpec("noalloc", seed, len(lengths), Hq, Hkv, D, dtype, bs,
                                    ("fixed", list(lengths)), new_tokens=("free", 0)))
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kernel,Hq,Hkv", [("valu", 8, 8), ("mfma", 16, 4)])
-def test_noalloc_two_calls_match_workspace_path(kernel, Hq, Hkv):
+@pytest.mark.parametrize("kernel,Hq,Hkv,D", [("valu", 8, 8, 128), ("mfma", 16, 4, 128),
+                                            ("mfma", 16, 4, 80)])
+def test_noalloc_two_calls_match_workspace_path(kernel, Hq, Hkv, D):
     import torch
     dev = need_gpu()
     lib = ops.load()
-    big = _case(400, (3000, 1, 17, 2049, 512, 777), Hq, Hkv)
-    small = _case(401, (100, 700, 5), Hq, Hkv)
+    big = _case(400, (3000, 1, 17, 2049, 512, 777), Hq, Hkv, D=D)
+    small = _case(401, (100, 700, 5), Hq, Hkv, D=D)
     for label, case, P in (("first (larger)", big, 256), ("second (smaller)", small, 64)):
         up = Uploaded(case, dev)
         sp = case.spec
-        need = lib.pa_decode_workspace_bytes(sp.num_seqs, Hq, Hkv, 128, 16, up.bt.shape[1], P)
-        say(f"noalloc {kernel} {label}: S={sp.num_seqs} Hq={Hq} Hkv={Hkv} P={P} "
+        need = lib.pa_decode_workspace_bytes(sp.num_seqs, Hq, Hkv, D, 16, up.bt.shape[1], P)
+        say(f"noalloc {kernel} {label}: S={sp.num_seqs} Hq={Hq} Hkv={Hkv} D={D} P={P} "
             f"partials={need} B")
         assert 0 < need <= SCRATCH_BYTES
         up.out.fill_(float("nan"))
